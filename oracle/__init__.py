@@ -1,0 +1,25 @@
+"""CPU oracle for chunk-wise block-causal wave attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+link this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+path (``block_causal_attention_wave_amd``) and imports nothing from it.
+
+Contents
+--------
+``oracle.plan``
+    Brute-force planner: builds the (chunk, level) update nodes, the context
+    lists from the policy phi(j, r), refresh nodes, the serial and the
+    pipelined ("wave") round assignment by round-by-round simulation, and a
+    naive liveness-based physical slot allocation.
+``oracle.attention``
+    fp64 softmax attention under an explicit dense additive mask, and the
+    round-to-nearest-even conversion of fp32 values to bfloat16.
+``oracle.rollout``
+    Serial rollout: executes a plan round by round against a dict cache keyed
+    by logical slot, recomputing every node's context from phi.
+
+Pins (values this oracle is checked against, other than itself) live in
+``tests/test_oracle_*.py`` and ``tests/golden/``.  Every function here is
+pinned; none is "parity unpinned".
+"""

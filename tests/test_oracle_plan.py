@@ -1,0 +1,256 @@
+"""Pins of the oracle planner against what the pages and plain reasoning fix.
+
+* phi: Table 1 of the arXiv 2609.22283 listing (golden table).
+* Round counts: Figure 2 of the same listing -- pipelined B+K-1 rounds,
+  serial B*K, both with the same B*K chunk-level updates.
+* No reverse dependencies (aipulsen.com Wave Forcing article).
+* Clean history is fully denoised (arXiv 2609.22283 listing, abstract).
+* Minimality of the pipelined round count by exhaustive search (tiny B, K).
+* Slot allocation: no two live slots share an id, and the capacity equals the
+  largest number of slots live at once (greedy interval colouring in order of
+  start time is optimal).
+"""
+import itertools
+import os
+
+import pytest
+
+from oracle import plan as op
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+NAMES = {"clean": op.CLEAN, "same-level": op.SAME_LEVEL, "progressive": op.PROGRESSIVE}
+
+
+def P(B, K, policy, sched=op.WAVE, H=-1, L=16, cond=0):
+    return op.Params(B=B, K=K, policy=policy, sched=sched, history_cap=H,
+                     chunk_len=L, cond_len=cond)
+
+
+def test_phi_golden_table():
+    n = 0
+    with open(os.path.join(GOLD, "phi_policies.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            pol, j, r, lv = line.split()
+            assert op.phi(NAMES[pol], int(j), int(r)) == int(lv), line
+            n += 1
+    assert n >= 12
+
+
+@pytest.mark.parametrize("B", [1, 2, 3, 5, 7, 9])
+@pytest.mark.parametrize("K", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("policy", [op.CLEAN, op.SAME_LEVEL, op.PROGRESSIVE])
+def test_round_counts_figure2(B, K, policy):
+    wave = op.oracle_plan(P(B, K, policy, op.WAVE))
+    serial = op.oracle_plan(P(B, K, policy, op.SERIAL))
+    assert serial["num_rounds"] == B * K
+    if policy == op.CLEAN and B > 1:
+        # Clean history must wait for the refreshed (fully denoised) previous
+        # chunk, so pipelining cannot overlap chunks.
+        assert wave["num_rounds"] == B * K
+    else:
+        assert wave["num_rounds"] == B + K - 1
+    for pl in (wave, serial):
+        ups = [(n[0], n[1]) for n in pl["nodes"] if n[2] == op.UPDATE]
+        assert sorted(ups) == sorted((i, j) for i in range(B) for j in range(1, K + 1))
+    # The staggered schedule of Figure 2(b): U(i, j) runs in round i + K - j.
+    if policy != op.CLEAN:
+        for n in wave["nodes"]:
+            if n[2] == op.UPDATE:
+                assert n[3] == n[0] + K - n[1]
+    for n in serial["nodes"]:
+        if n[2] == op.UPDATE:
+            assert n[3] == n[0] * K + K - n[1]
+
+
+@pytest.mark.parametrize("policy", [op.CLEAN, op.SAME_LEVEL, op.PROGRESSIVE])
+@pytest.mark.parametrize("sched", [op.SERIAL, op.WAVE])
+@pytest.mark.parametrize("H", [-1, 0, 1, 2, 6])
+@pytest.mark.parametrize("cond", [0, 5])
+def test_structure(policy, sched, H, cond):
+    B, K = 8, 3
+    pl = op.oracle_plan(P(B, K, policy, sched, H=H, cond=cond))
+    nodes, ctx, writes = pl["nodes"], pl["ctx"], pl["writes"]
+    for (c, lv, kind, t, qo, ql, cb, cc, wb, wc) in nodes:
+        refs = ctx[cb:cb + cc]
+        # No reverse dependencies: nothing from a later chunk.
+        assert all(r[0] <= c for r in refs)
+        # Own slot last.
+        assert (refs[-1][0], refs[-1][1]) == (c, lv)
+        # History window.
+        if H >= 0:
+            assert all(c - r[0] <= H for r in refs)
+        hist = [r for r in refs if r[0] < c and r[1] != op.COND]
+        if policy == op.CLEAN:
+            assert all(r[1] == 0 for r in hist)  # fully denoised history
+        if kind == op.REFRESH:
+            assert lv == 0 and all(r[1] == 0 for r in hist)
+        # Closer history is never cleaner than farther history (the
+        # clean-to-noisy frontier of the aipulsen.com article).
+        levels = [r[1] for r in hist]
+        assert levels == sorted(levels)
+        # Conditioning slots: one per history chunk, right before its latent.
+        if cond:
+            for a, b in zip(refs, refs[1:]):
+                if a[1] == op.COND:
+                    assert b[0] == a[0] and b[1] != op.COND
+    # Every read slot is written exactly once, before (or, from a lower
+    # chunk, in the same round as) its read.
+    wr = {}
+    for (c, lv, kind, t, qo, ql, cb, cc, wb, wc) in nodes:
+        for w in writes[wb:wb + wc]:
+            assert (w[0], w[1]) not in wr
+            wr[(w[0], w[1])] = (t, c)
+    for (c, lv, kind, t, qo, ql, cb, cc, wb, wc) in nodes:
+        for r in ctx[cb:cb + cc]:
+            wt, wch = wr[(r[0], r[1])]
+            assert wt < t or (wt == t and wch <= c)
+
+
+def _live_intervals(pl):
+    first, last = {}, {}
+    for (c, lv, kind, t, qo, ql, cb, cc, wb, wc) in pl["nodes"]:
+        for w in pl["writes"][wb:wb + wc]:
+            first[(w[0], w[1])] = t
+        for r in pl["ctx"][cb:cb + cc]:
+            last[(r[0], r[1])] = max(last.get((r[0], r[1]), -1), t)
+    return first, last
+
+
+@pytest.mark.parametrize("policy", [op.CLEAN, op.SAME_LEVEL, op.PROGRESSIVE])
+@pytest.mark.parametrize("sched", [op.SERIAL, op.WAVE])
+@pytest.mark.parametrize("H,cond", [(-1, 0), (2, 0), (6, 3), (-1, 3)])
+def test_allocation_valid_and_minimal(policy, sched, H, cond):
+    pl = op.oracle_plan(P(9, 4, policy, sched, H=H, cond=cond))
+    first, last = _live_intervals(pl)
+    phys = {}
+    for w in pl["writes"]:
+        phys[(w[0], w[1])] = w[2]
+    for r in pl["ctx"]:
+        assert phys[(r[0], r[1])] == r[2]
+    slots = list(first)
+    for a, b in itertools.combinations(slots, 2):
+        overlap = not (last[a] < first[b] or last[b] < first[a])
+        if overlap:
+            assert phys[a] != phys[b], (a, b)
+    max_live = max(sum(1 for s in slots if first[s] <= t <= last[s])
+                   for t in range(pl["num_rounds"]))
+    assert pl["num_phys_slots"] == max_live
+
+
+def _min_rounds_bruteforce(p):
+    """Smallest R admitting any legal round assignment, by exhaustive DFS."""
+    per_chunk = op.build_nodes(p)
+    order = [n for i in range(p.B) for n in per_chunk[i]]
+    writer = {}
+    for n in order:
+        for s in n.writes:
+            writer[s] = n
+    remaining_after = {}
+    for i in range(p.B):
+        lst = per_chunk[i]
+        for k, n in enumerate(lst):
+            remaining_after[id(n)] = len(lst) - 1 - k
+
+    def feasible(R):
+        rounds = {}
+
+        def dfs(idx):
+            if idx == len(order):
+                return True
+            n = order[idx]
+            lst = per_chunk[n.chunk]
+            k = lst.index(n)
+            lo = n.chunk if k == 0 else rounds[id(lst[k - 1])] + 1
+            hi = R - 1 - remaining_after[id(n)]
+            for t in range(lo, hi + 1):
+                ok = True
+                for s in n.ctx:
+                    if s in n.writes:
+                        continue
+                    w = writer[s]
+                    wt = rounds[id(w)]
+                    if not (wt < t or (wt == t and w.chunk < n.chunk)):
+                        ok = False
+                        break
+                if ok:
+                    rounds[id(n)] = t
+                    if dfs(idx + 1):
+                        return True
+                    del rounds[id(n)]
+            return False
+
+        return dfs(0)
+
+    R = 1
+    while not feasible(R):
+        R += 1
+    return R
+
+
+@pytest.mark.parametrize("B", [1, 2, 3])
+@pytest.mark.parametrize("K", [1, 2, 3])
+@pytest.mark.parametrize("policy", [op.CLEAN, op.SAME_LEVEL, op.PROGRESSIVE])
+def test_wave_rounds_minimal_bruteforce(B, K, policy):
+    p = P(B, K, policy, op.WAVE)
+    assert op.oracle_plan(p)["num_rounds"] == _min_rounds_bruteforce(p)
+
+
+def _parse_plan_fixture(name):
+    rows = []
+    with open(os.path.join(GOLD, name)) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            head, tail = line.split(":")
+            t, kind, c, lv, pid = head.split()
+            refs = []
+            for tok in tail.split():
+                cl, ph = tok.split("@")
+                a, b = cl.split(".")
+                refs.append((int(a), int(b), int(ph)))
+            rows.append((int(t), kind, int(c), int(lv), int(pid), refs))
+    return rows
+
+
+def test_tiny_progressive_worked_plan():
+    pl = op.oracle_plan(P(4, 2, op.PROGRESSIVE, op.WAVE, L=128))
+    rows = _parse_plan_fixture("plan_tiny_progressive.txt")
+    assert pl["num_rounds"] == 5 and pl["num_phys_slots"] == 4
+    assert len(rows) == len(pl["nodes"])
+    for row, n in zip(rows, pl["nodes"]):
+        t, kind, c, lv, pid, refs = row
+        assert (n[3], n[2], n[0], n[1]) == (t, op.REFRESH if kind == "R" else op.UPDATE, c, lv)
+        w = pl["writes"][n[8]:n[8] + n[9]]
+        assert [x[2] for x in w] == [pid]
+        got = [(x[0], x[1], x[2]) for x in pl["ctx"][n[6]:n[6] + n[7]]]
+        assert got == refs
+
+
+def test_planted_mistakes_are_caught(monkeypatch):
+    """A plausible slip in phi (off-by-one, sign) breaks a page pin."""
+    orig = op.phi
+    broken = {
+        "progressive uses j-r+1": lambda pol, j, r: max(j - r + 1, 0) if pol == op.PROGRESSIVE else orig(pol, j, r),
+        "progressive uses j+r": lambda pol, j, r: (j + r) if pol == op.PROGRESSIVE else orig(pol, j, r),
+        "same-level reads j+1": lambda pol, j, r: (j + 1) if pol == op.SAME_LEVEL else orig(pol, j, r),
+    }
+    for name, fn in broken.items():
+        monkeypatch.setattr(op, "phi", fn)
+        failed = False
+        try:
+            for pol in (op.SAME_LEVEL, op.PROGRESSIVE):
+                pl = op.oracle_plan(P(5, 3, pol, op.WAVE))
+                if pl["num_rounds"] != 5 + 3 - 1:
+                    failed = True
+        except Exception:
+            failed = True
+        if not failed:
+            # golden table must catch it then
+            try:
+                test_phi_golden_table()
+            except AssertionError:
+                failed = True
+        assert failed, name
+    monkeypatch.setattr(op, "phi", orig)
