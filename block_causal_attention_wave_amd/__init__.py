@@ -1,0 +1,189 @@
+"""Chunk-wise block-causal wave attention on AMD MI355X (gfx950).
+
+Thin Python binding of ``include/wave.h`` (libwave.so): argument marshalling
+only.  PyTorch supplies device memory and streams; every step of the path
+(planning, K/V cache writes, attention) runs in the native library.  There is
+no fallback: if libwave.so is missing, importing the binding functions raises.
+
+    plan  = wave_plan(B=7, K=4, policy=PROGRESSIVE, sched=WAVE, chunk_len=4680)
+    desc  = plan.upload(device)
+    cache = KVCache(plan.num_phys_slots, heads=12, head_dim=128,
+                    lpad=plan.lpad(), device=device)
+    for t in range(plan.num_rounds):
+        kv_write(plan, desc, t, cache, k_fresh[t], v_fresh[t])
+        o, lse = wave_attn(plan, desc, t, cache, q[t], scale=128 ** -0.5)
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import numpy as np
+
+from . import _lib
+from ._lib import (WAVE_CLEAN, WAVE_DTYPE_BF16, WAVE_DTYPE_FP32, WAVE_KEY_TILE, WAVE_LEVEL_COND,
+                   WAVE_NODE_REFRESH, WAVE_NODE_UPDATE, WAVE_PROGRESSIVE, WAVE_Q_TILE,
+                   WAVE_SAME_LEVEL, WAVE_SCHED_SERIAL, WAVE_SCHED_WAVE, WaveError)
+
+CLEAN, SAME_LEVEL, PROGRESSIVE = WAVE_CLEAN, WAVE_SAME_LEVEL, WAVE_PROGRESSIVE
+SERIAL, WAVE = WAVE_SCHED_SERIAL, WAVE_SCHED_WAVE
+
+__all__ = ["Plan", "KVCache", "wave_plan", "kv_write", "wave_attn", "WaveError",
+           "CLEAN", "SAME_LEVEL", "PROGRESSIVE", "SERIAL", "WAVE", "WAVE_LEVEL_COND",
+           "WAVE_Q_TILE", "WAVE_KEY_TILE", "WAVE_NODE_UPDATE", "WAVE_NODE_REFRESH"]
+
+
+def _arr(ptr, n, cols):
+    if n == 0:
+        return np.zeros((0, cols) if cols else (0,), dtype=np.int32)
+    buf = C.cast(ptr, C.POINTER(C.c_int32 * (n * (cols or 1)))).contents
+    a = np.frombuffer(buf, dtype=np.int32).copy()
+    return a.reshape(n, cols) if cols else a
+
+
+class Plan:
+    """A host plan (``wave_plan``) with numpy copies of its view arrays.
+
+    nodes : [N, 10] chunk, level, kind, round, q_offset, q_len, ctx_begin,
+            ctx_count, write_begin, write_count
+    ctx, writes : [*, 4] chunk, level, phys_slot, len
+    work : [*, 4] node, q_start, q_rows, keys
+    """
+
+    def __init__(self, B, K, policy, sched, chunk_len, history_cap=-1, cond_len=0, q_tile=0):
+        lib = _lib.load()
+        self.params = dict(B=B, K=K, policy=policy, sched=sched, history_cap=history_cap,
+                           chunk_len=chunk_len, cond_len=cond_len, q_tile=q_tile)
+        p = _lib.PlanParams(B, K, policy, sched, history_cap, chunk_len, cond_len, q_tile)
+        h = C.c_void_p()
+        _lib.check(lib.wave_plan(C.byref(p), C.byref(h)))
+        self._h = h
+        v = _lib.PlanView()
+        _lib.check(lib.wave_plan_view_get(h, C.byref(v)))
+        self.num_rounds = v.num_rounds
+        self.num_phys_slots = v.num_phys_slots
+        self.max_slot_len = v.max_slot_len
+        self.q_tile = v.q_tile
+        self.round_node_begin = _arr(v.round_node_begin, v.num_rounds + 1, 0)
+        self.round_write_begin = _arr(v.round_write_begin, v.num_rounds + 1, 0)
+        self.round_work_begin = _arr(v.round_work_begin, v.num_rounds + 1, 0)
+        self.round_q_rows = _arr(v.round_q_rows, v.num_rounds, 0)
+        self.round_src_rows = _arr(v.round_src_rows, v.num_rounds, 0)
+        self.nodes = _arr(v.nodes, v.num_nodes, 10)
+        self.ctx = _arr(v.ctx, v.num_ctx, 4)
+        self.writes = _arr(v.writes, v.num_writes, 4)
+        self.work = _arr(v.work, v.num_work, 4)
+        size = C.c_size_t()
+        _lib.check(lib.wave_plan_desc_size(h, C.byref(size)))
+        self._desc = np.zeros(size.value // 4, dtype=np.int32)
+        _lib.check(lib.wave_plan_desc_pack(h, self._desc.ctypes.data_as(C.c_void_p), size.value))
+
+    @property
+    def handle(self):
+        return self._h
+
+    def desc(self) -> np.ndarray:
+        return self._desc.copy()
+
+    def upload(self, device):
+        import torch
+        return torch.from_numpy(self._desc.copy()).to(device)
+
+    def lpad(self) -> int:
+        return -(-self.max_slot_len // WAVE_KEY_TILE) * WAVE_KEY_TILE
+
+    def round_nodes(self, t):
+        return self.nodes[self.round_node_begin[t]:self.round_node_begin[t + 1]]
+
+    def round_writes(self, t):
+        return self.writes[self.round_write_begin[t]:self.round_write_begin[t + 1]]
+
+    def node_ctx(self, n):
+        return self.ctx[n[6]:n[6] + n[7]]
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            _lib.load().wave_plan_destroy(h)
+            self._h = None
+
+
+def wave_plan(**kw) -> Plan:
+    return Plan(**kw)
+
+
+class KVCache:
+    """One layer's cache: K [slots][heads][lpad][d] and V^T [slots][heads][d][lpad], bf16."""
+
+    def __init__(self, num_slots, heads, head_dim, lpad, device, fill=None):
+        import torch
+        self.k = torch.empty((num_slots, heads, lpad, head_dim), dtype=torch.bfloat16, device=device)
+        self.vt = torch.empty((num_slots, heads, head_dim, lpad), dtype=torch.bfloat16, device=device)
+        if fill is not None:
+            self.k.fill_(fill)
+            self.vt.fill_(fill)
+        self.num_slots, self.heads, self.head_dim, self.lpad = num_slots, heads, head_dim, lpad
+        self._c = _lib.KvCache(self.k.data_ptr(), self.vt.data_ptr(), num_slots, heads, head_dim, lpad)
+
+    @property
+    def c(self):
+        return self._c
+
+
+def _stream_ptr(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return WAVE_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return WAVE_DTYPE_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check_rows(t, rows, heads, head_dim, what):
+    if t.dim() != 3 or t.shape[0] != rows or t.shape[1] != heads or t.shape[2] != head_dim:
+        raise ValueError(f"{what}: expected [{rows}, {heads}, {head_dim}], got {tuple(t.shape)}")
+    if t.stride(2) != 1 or t.stride(1) != head_dim:
+        raise ValueError(f"{what}: heads and head_dim must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{what}: must be a device tensor")
+
+
+def kv_write(plan: Plan, d_desc, round: int, cache: KVCache, k_src, v_src, stream=None) -> None:
+    """Write round `round`'s fresh K/V ([rows, heads, d], bf16 or fp32) into `cache`."""
+    rows = int(plan.round_src_rows[round]) if 0 <= round < plan.num_rounds else 0
+    _check_rows(k_src, rows, cache.heads, cache.head_dim, "k_src")
+    _check_rows(v_src, rows, cache.heads, cache.head_dim, "v_src")
+    if k_src.dtype != v_src.dtype or k_src.stride(0) != v_src.stride(0):
+        raise ValueError("k_src and v_src must share dtype and row stride")
+    _lib.check(_lib.load().kv_write(plan.handle, C.c_void_p(d_desc.data_ptr()), round, C.byref(cache.c),
+                                    C.c_void_p(k_src.data_ptr()), C.c_void_p(v_src.data_ptr()),
+                                    _dtype_code(k_src), k_src.stride(0), _stream_ptr(stream)))
+
+
+def wave_attn(plan: Plan, d_desc, round: int, cache: KVCache, q, scale: float, o=None, lse=None,
+              want_lse=True, stream=None):
+    """Attention of round `round`: q [rows, heads, d] (bf16 or fp32) -> (o bf16, lse fp32 [heads, rows])."""
+    import torch
+    rows = int(plan.round_q_rows[round]) if 0 <= round < plan.num_rounds else 0
+    _check_rows(q, rows, cache.heads, cache.head_dim, "q")
+    if o is None:
+        o = torch.empty((rows, cache.heads, cache.head_dim), dtype=torch.bfloat16, device=q.device)
+    elif o.dtype != torch.bfloat16 or not o.is_contiguous() or tuple(o.shape) != (rows, cache.heads, cache.head_dim):
+        raise ValueError("o must be a contiguous bf16 [rows, heads, d] tensor")
+    if lse is None and want_lse:
+        lse = torch.empty((cache.heads, rows), dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                              or tuple(lse.shape) != (cache.heads, rows)):
+        raise ValueError("lse must be a contiguous fp32 [heads, rows] tensor")
+    _lib.check(_lib.load().wave_attn(plan.handle, C.c_void_p(d_desc.data_ptr()), round, C.byref(cache.c),
+                                     C.c_void_p(q.data_ptr()), _dtype_code(q), q.stride(0),
+                                     C.c_void_p(o.data_ptr()),
+                                     C.c_void_p(lse.data_ptr() if lse is not None else 0),
+                                     float(scale), _stream_ptr(stream)))
+    return o, lse

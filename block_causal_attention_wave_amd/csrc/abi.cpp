@@ -1,0 +1,202 @@
+// C ABI shim: argument validation, error reporting and kernel launches.
+// No C++ exception crosses this boundary; every entry point returns a status.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "kernels.hpp"
+#include "planner.hpp"
+#include "wave.h"
+
+struct wave_plan {
+  wave::Plan p;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t set_error(int32_t code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int32_t ok() {
+  g_last_error.clear();
+  return WAVE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks shared by kv_write and wave_attn.
+int32_t check_common(const wave_plan_t* plan, const void* d_desc, int32_t round,
+                     const wave_kv_cache* cache, const char* fn) {
+  const std::string f(fn);
+  if (!plan || !d_desc || !cache) return set_error(WAVE_ERR_INVALID_ARG, f + ": null plan, descriptor or cache");
+  const wave::Plan& p = plan->p;
+  if (round < 0 || round >= p.num_rounds())
+    return set_error(WAVE_ERR_INVALID_ARG, f + ": round out of range");
+  if (!cache->k || !cache->vt) return set_error(WAVE_ERR_INVALID_ARG, f + ": null cache buffer");
+  if (!aligned16(cache->k) || !aligned16(cache->vt) || !aligned16(d_desc))
+    return set_error(WAVE_ERR_INVALID_ARG, f + ": cache buffers and descriptor must be 16-byte aligned");
+  if (cache->head_dim != 64 && cache->head_dim != 128)
+    return set_error(WAVE_ERR_UNSUPPORTED, f + ": head_dim must be 64 or 128");
+  if (cache->heads < 1 || cache->heads > 65535) return set_error(WAVE_ERR_INVALID_ARG, f + ": heads out of range");
+  if (cache->lpad < 1 || cache->lpad % WAVE_KEY_TILE != 0)
+    return set_error(WAVE_ERR_INVALID_ARG, f + ": lpad must be a positive multiple of WAVE_KEY_TILE");
+  if (cache->lpad < p.max_slot_len)
+    return set_error(WAVE_ERR_CAPACITY, f + ": lpad shorter than the plan's longest slot");
+  if (cache->num_slots < p.num_phys_slots)
+    return set_error(WAVE_ERR_CAPACITY, f + ": cache has fewer slots than the plan needs");
+  return WAVE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t wave_plan(const wave_plan_params* params, wave_plan_t** out) {
+  if (!params || !out) return set_error(WAVE_ERR_INVALID_ARG, "wave_plan: null argument");
+  *out = nullptr;
+  try {
+    wave_plan_t* h = new wave_plan_t();
+    std::string err;
+    const int32_t rc = wave::build_plan(*params, h->p, &err);
+    if (rc != WAVE_OK) {
+      delete h;
+      return set_error(rc, err);
+    }
+    *out = h;
+    return ok();
+  } catch (const std::bad_alloc&) {
+    return set_error(WAVE_ERR_NOMEM, "wave_plan: out of host memory");
+  } catch (...) {
+    return set_error(WAVE_ERR_INVALID_ARG, "wave_plan: unexpected failure");
+  }
+}
+
+int32_t wave_plan_view_get(const wave_plan_t* plan, wave_plan_view* out) {
+  if (!plan || !out) return set_error(WAVE_ERR_INVALID_ARG, "wave_plan_view_get: null argument");
+  const wave::Plan& p = plan->p;
+  out->num_rounds = p.num_rounds();
+  out->num_nodes = static_cast<int32_t>(p.nodes.size());
+  out->num_ctx = static_cast<int32_t>(p.ctx.size());
+  out->num_writes = static_cast<int32_t>(p.writes.size());
+  out->num_work = static_cast<int32_t>(p.work.size());
+  out->num_phys_slots = p.num_phys_slots;
+  out->max_slot_len = p.max_slot_len;
+  out->q_tile = p.params.q_tile;
+  out->round_node_begin = p.round_node_begin.data();
+  out->round_write_begin = p.round_write_begin.data();
+  out->round_work_begin = p.round_work_begin.data();
+  out->round_q_rows = p.round_q_rows.data();
+  out->round_src_rows = p.round_src_rows.data();
+  out->nodes = p.nodes.data();
+  out->ctx = p.ctx.data();
+  out->writes = p.writes.data();
+  out->work = p.work.data();
+  return ok();
+}
+
+int32_t wave_plan_desc_size(const wave_plan_t* plan, size_t* bytes) {
+  if (!plan || !bytes) return set_error(WAVE_ERR_INVALID_ARG, "wave_plan_desc_size: null argument");
+  *bytes = plan->p.desc.size() * sizeof(int32_t);
+  return ok();
+}
+
+int32_t wave_plan_desc_pack(const wave_plan_t* plan, void* host_dst, size_t bytes) {
+  if (!plan || !host_dst) return set_error(WAVE_ERR_INVALID_ARG, "wave_plan_desc_pack: null argument");
+  const size_t need = plan->p.desc.size() * sizeof(int32_t);
+  if (bytes < need) return set_error(WAVE_ERR_INVALID_ARG, "wave_plan_desc_pack: destination too small");
+  std::memcpy(host_dst, plan->p.desc.data(), need);
+  return ok();
+}
+
+void wave_plan_destroy(wave_plan_t* plan) { delete plan; }
+
+int32_t kv_write(const wave_plan_t* plan, const void* d_desc, int32_t round, const wave_kv_cache* cache,
+                 const void* k_src, const void* v_src, int32_t src_dtype, int64_t src_row_stride,
+                 void* stream) {
+  int32_t rc = check_common(plan, d_desc, round, cache, "kv_write");
+  if (rc != WAVE_OK) return rc;
+  const wave::Plan& p = plan->p;
+  const int32_t w0 = p.round_write_begin[round], w1 = p.round_write_begin[round + 1];
+  if (w1 == w0) return ok();
+  if (!k_src || !v_src) return set_error(WAVE_ERR_INVALID_ARG, "kv_write: null source");
+  if (src_dtype != WAVE_DTYPE_BF16 && src_dtype != WAVE_DTYPE_FP32)
+    return set_error(WAVE_ERR_UNSUPPORTED, "kv_write: src_dtype must be WAVE_DTYPE_BF16 or WAVE_DTYPE_FP32");
+  const int64_t row = static_cast<int64_t>(cache->heads) * cache->head_dim;
+  if (src_row_stride < row) return set_error(WAVE_ERR_INVALID_ARG, "kv_write: src_row_stride < heads*head_dim");
+  const int64_t esz = src_dtype == WAVE_DTYPE_FP32 ? 4 : 2;
+  if (!aligned16(k_src) || !aligned16(v_src) || (src_row_stride * esz) % 16 != 0)
+    return set_error(WAVE_ERR_UNSUPPORTED, "kv_write: sources and row stride must be 16-byte aligned");
+  const int32_t* desc = static_cast<const int32_t*>(d_desc);
+  wave::KvWriteArgs a{};
+  a.writes = desc + p.desc[10] + static_cast<int64_t>(w0) * wave::kWriteStride;
+  a.num_writes = w1 - w0;
+  a.k = cache->k;
+  a.vt = cache->vt;
+  a.heads = cache->heads;
+  a.head_dim = cache->head_dim;
+  a.lpad = cache->lpad;
+  a.k_src = k_src;
+  a.v_src = v_src;
+  a.src_fp32 = src_dtype == WAVE_DTYPE_FP32;
+  a.src_row_stride = src_row_stride;
+  const hipError_t e = wave::launch_kv_write(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return set_error(WAVE_ERR_HIP, std::string("kv_write: ") + hipGetErrorString(e));
+  return ok();
+}
+
+int32_t wave_attn(const wave_plan_t* plan, const void* d_desc, int32_t round, const wave_kv_cache* cache,
+                  const void* q, int32_t q_dtype, int64_t q_row_stride, void* o, float* lse, float scale,
+                  void* stream) {
+  int32_t rc = check_common(plan, d_desc, round, cache, "wave_attn");
+  if (rc != WAVE_OK) return rc;
+  const wave::Plan& p = plan->p;
+  if (!q || !o) return set_error(WAVE_ERR_INVALID_ARG, "wave_attn: null q or o");
+  if (p.params.q_tile != WAVE_Q_TILE)
+    return set_error(WAVE_ERR_UNSUPPORTED, "wave_attn: plan q_tile must be WAVE_Q_TILE");
+  if (p.max_ctx > 512) return set_error(WAVE_ERR_UNSUPPORTED, "wave_attn: gather lists longer than 512 slots");
+  if (q_dtype != WAVE_DTYPE_BF16 && q_dtype != WAVE_DTYPE_FP32)
+    return set_error(WAVE_ERR_UNSUPPORTED, "wave_attn: q_dtype must be WAVE_DTYPE_BF16 or WAVE_DTYPE_FP32");
+  const int64_t row = static_cast<int64_t>(cache->heads) * cache->head_dim;
+  if (q_row_stride < row) return set_error(WAVE_ERR_INVALID_ARG, "wave_attn: q_row_stride < heads*head_dim");
+  const int64_t esz = q_dtype == WAVE_DTYPE_FP32 ? 4 : 2;
+  if (!aligned16(q) || (q_row_stride * esz) % 16 != 0 || (reinterpret_cast<uintptr_t>(o) & 7u) != 0 ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0))
+    return set_error(WAVE_ERR_UNSUPPORTED, "wave_attn: q must be 16-byte aligned (rows too), o 8-byte, lse 4-byte");
+  if (!std::isfinite(scale)) return set_error(WAVE_ERR_INVALID_ARG, "wave_attn: scale must be finite");
+  const int32_t k0 = p.round_work_begin[round], k1 = p.round_work_begin[round + 1];
+  if (static_cast<int64_t>(k1 - k0) * cache->heads > INT32_MAX)
+    return set_error(WAVE_ERR_UNSUPPORTED, "wave_attn: too many work items");
+  const int32_t* desc = static_cast<const int32_t*>(d_desc);
+  wave::AttnArgs a{};
+  a.nodes = desc + p.desc[8];
+  a.ctx = desc + p.desc[9];
+  a.work = desc + p.desc[11];
+  a.work_begin = k0;
+  a.num_work = k1 - k0;
+  a.k = cache->k;
+  a.vt = cache->vt;
+  a.heads = cache->heads;
+  a.head_dim = cache->head_dim;
+  a.lpad = cache->lpad;
+  a.q = q;
+  a.q_fp32 = q_dtype == WAVE_DTYPE_FP32;
+  a.q_row_stride = q_row_stride;
+  a.o = o;
+  a.lse = lse;
+  a.lse_stride = p.round_q_rows[round];
+  a.scale_log2e = scale * 1.4426950408889634f;
+  const hipError_t e = wave::launch_wave_attn(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return set_error(WAVE_ERR_HIP, std::string("wave_attn: ") + hipGetErrorString(e));
+  return ok();
+}
+
+const char* wave_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

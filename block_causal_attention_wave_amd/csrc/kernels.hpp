@@ -1,0 +1,46 @@
+// Launch interfaces of the gfx950 kernels (host side).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+namespace wave {
+
+// One round's K/V write.  `writes` points at the round's rows of the write
+// table in the device descriptor (phys_slot, len, src_offset, 0 per row).
+struct KvWriteArgs {
+  const int32_t* writes;
+  int32_t num_writes;
+  void* k;
+  void* vt;
+  int32_t heads, head_dim, lpad;
+  const void* k_src;
+  const void* v_src;
+  int32_t src_fp32;
+  int64_t src_row_stride;  // elements
+};
+
+// One round's attention.  Table pointers are the descriptor's node, ctx and
+// work tables; the round's items are work[work_begin .. work_begin+num_work).
+struct AttnArgs {
+  const int32_t* nodes;
+  const int32_t* ctx;
+  const int32_t* work;
+  int32_t work_begin, num_work;
+  const void* k;
+  const void* vt;
+  int32_t heads, head_dim, lpad;
+  const void* q;
+  int32_t q_fp32;
+  int64_t q_row_stride;  // elements
+  void* o;
+  float* lse;
+  int32_t lse_stride;  // rows of the round (LSE is [heads][rows])
+  float scale_log2e;   // scale * log2(e)
+};
+
+hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
+hipError_t launch_wave_attn(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace wave

@@ -1,0 +1,196 @@
+/*
+ * wave.h -- C ABI of chunk-wise block-causal "wave" attention on AMD gfx950.
+ *
+ * What the calls compute
+ * ----------------------
+ * A streaming video diffusion model denoises B chunks through K levels.  The
+ * update of chunk i at level j attends to its own tokens (both directions)
+ * and to the K/V of earlier chunks, never later ones; which level of each
+ * earlier chunk it reads is set by a context policy phi(j, r) of the level j
+ * and the chunk distance r (streaming-video-diffusion design-space paper,
+ * thelatestinai.com listing of arXiv 2609.22283: Figure 1, Table 1):
+ *   clean        phi = 0             (fully denoised history)
+ *   same-level   phi = j
+ *   progressive  phi = max(j - r, 0)
+ * Run serially, the B*K updates take B*K rounds; pipelined, chunks sit at
+ * staggered levels and the same B*K updates take B+K-1 rounds (same paper,
+ * Figure 2).  Wave Forcing (aiany.app summary, mechanism paragraph) hands K/V
+ * to later chunks early, within the round; Wan-Streamer v0.2 (abstract) writes
+ * incoming K/V into a cache and passes language/state to the generator only as
+ * a K/V slice (here: an optional per-chunk conditioning slot).
+ *
+ *   wave_plan   (host)   builds the (chunk, level) nodes, their gather lists
+ *                        (context slots in timeline order), the rounds, the
+ *                        physical cache slots and a packed device descriptor.
+ *   kv_write    (device) copies one round's fresh K/V into the cache slots.
+ *   wave_attn   (device) block-causal flash attention of one round: every
+ *                        query chunk of the round against exactly the slots of
+ *                        its gather list; masked slots are never read.
+ *
+ * Conventions
+ * -----------
+ * Levels: 0 = clean, K = pure noise.  Update U(i, j), j = K..1, consumes
+ * chunk i at level j and writes slot (i, j).  The clean slot (i, 0) is written
+ * by a refresh node R(i) (a forward pass over the finished chunk), created
+ * only when some node reads (i, 0).  A conditioning slot C(i) (level
+ * WAVE_LEVEL_COND) is written with chunk i's first update when cond_len > 0.
+ * A node may read a slot written in an earlier round, or earlier in the same
+ * round by a lower chunk: each round's kv_write precedes its wave_attn.
+ *
+ * All int32 status returns: WAVE_OK or a negative WAVE_ERR_*; the message of
+ * the last failure on the calling thread is returned by wave_last_error().
+ * No C++ exception crosses this boundary.  The library never allocates or
+ * frees device memory: every device buffer belongs to the caller.
+ */
+#ifndef WAVE_H
+#define WAVE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  WAVE_OK = 0,
+  WAVE_ERR_INVALID_ARG = -1, /* null pointer, out-of-range value, bad round */
+  WAVE_ERR_CAPACITY = -2,    /* cache has fewer slots / shorter lpad than the plan needs */
+  WAVE_ERR_UNSUPPORTED = -3, /* head_dim, dtype or q_tile the kernels do not handle */
+  WAVE_ERR_HIP = -4,         /* a HIP launch reported an error */
+  WAVE_ERR_NOMEM = -5        /* host allocation failed */
+};
+
+enum { WAVE_CLEAN = 0, WAVE_SAME_LEVEL = 1, WAVE_PROGRESSIVE = 2 };
+enum { WAVE_SCHED_SERIAL = 0, WAVE_SCHED_WAVE = 1 };
+enum { WAVE_NODE_UPDATE = 0, WAVE_NODE_REFRESH = 1 };
+enum { WAVE_DTYPE_BF16 = 0, WAVE_DTYPE_FP32 = 1 };
+#define WAVE_LEVEL_COND (-1)
+
+/* Query rows per attention work item; wave_attn handles this value only. */
+#define WAVE_Q_TILE 256
+/* Keys per streamed K/V tile; cache lpad must be a multiple of it. */
+#define WAVE_KEY_TILE 64
+
+typedef struct wave_plan_params {
+  int32_t B;           /* chunks, >= 1 */
+  int32_t K;           /* denoising levels (updates per chunk), >= 1 */
+  int32_t policy;      /* WAVE_CLEAN / WAVE_SAME_LEVEL / WAVE_PROGRESSIVE */
+  int32_t sched;       /* WAVE_SCHED_SERIAL / WAVE_SCHED_WAVE */
+  int32_t history_cap; /* H: earlier chunks visible, -1 = all, >= 0 = the last H */
+  int32_t chunk_len;   /* tokens per chunk: query rows of a node, length of its slot, >= 1 */
+  int32_t cond_len;    /* tokens of each conditioning slot C(i); 0 = no conditioning */
+  int32_t q_tile;      /* query rows per work item; 0 = WAVE_Q_TILE */
+} wave_plan_params;
+
+/* One logical cache slot as referenced by a node. */
+typedef struct wave_slot_ref {
+  int32_t chunk;     /* chunk index */
+  int32_t level;     /* 0..K, or WAVE_LEVEL_COND */
+  int32_t phys_slot; /* physical slot index in the per-layer cache */
+  int32_t len;       /* valid tokens in the slot (chunk_len or cond_len) */
+} wave_slot_ref;
+
+typedef struct wave_node {
+  int32_t chunk, level, kind, round;
+  int32_t q_offset;    /* first row of this node in the round's packed Q / O */
+  int32_t q_len;       /* query rows (= chunk_len) */
+  int32_t ctx_begin;   /* gather list: ctx[ctx_begin .. ctx_begin+ctx_count), timeline order, own slot last */
+  int32_t ctx_count;
+  int32_t write_begin; /* slots this node writes: writes[write_begin ..), conditioning first */
+  int32_t write_count;
+} wave_node;
+
+/* Attention work item: query rows [q_start, q_start+q_rows) of one node. */
+typedef struct wave_work {
+  int32_t node;    /* global node index */
+  int32_t q_start; /* row offset inside the node */
+  int32_t q_rows;  /* <= q_tile */
+  int32_t keys;    /* total keys over the node's gather list */
+} wave_work;
+
+/* Read-only view of a plan.  All arrays belong to the plan and stay valid
+ * until wave_plan_destroy.  Nodes are grouped by round, ascending chunk inside
+ * a round; writes and ctx entries are grouped by node in node order; a
+ * round's work items are sorted by decreasing cost. */
+typedef struct wave_plan_view {
+  int32_t num_rounds, num_nodes, num_ctx, num_writes, num_work;
+  int32_t num_phys_slots; /* cache slots per layer the plan needs */
+  int32_t max_slot_len;   /* longest slot, tokens */
+  int32_t q_tile;
+  const int32_t* round_node_begin;  /* [num_rounds+1] */
+  const int32_t* round_write_begin; /* [num_rounds+1] */
+  const int32_t* round_work_begin;  /* [num_rounds+1] */
+  const int32_t* round_q_rows;      /* [num_rounds]: rows of the round's packed Q / O */
+  const int32_t* round_src_rows;    /* [num_rounds]: rows of the round's packed fresh K/V */
+  const wave_node* nodes;
+  const wave_slot_ref* ctx;
+  const wave_slot_ref* writes;
+  const wave_work* work;
+} wave_plan_view;
+
+typedef struct wave_plan wave_plan_t;
+
+/* Build a plan on the host.  Deterministic: equal params give an identical
+ * view and descriptor.  *out receives a new plan owned by the caller (free
+ * with wave_plan_destroy); a plan is immutable and may be shared by threads. */
+int32_t wave_plan(const wave_plan_params* params, wave_plan_t** out);
+int32_t wave_plan_view_get(const wave_plan_t* plan, wave_plan_view* out);
+/* Size in bytes of the packed device descriptor (int32 words). */
+int32_t wave_plan_desc_size(const wave_plan_t* plan, size_t* bytes);
+/* Write the descriptor into host memory [host_dst, host_dst+bytes); the caller
+ * uploads it once to device memory and passes that pointer as d_desc. */
+int32_t wave_plan_desc_pack(const wave_plan_t* plan, void* host_dst, size_t bytes);
+void wave_plan_destroy(wave_plan_t* plan);
+
+/* Per-layer K/V cache, device memory owned by the caller.
+ *   k : bf16 [num_slots][heads][lpad][head_dim]  (token-major per head)
+ *   vt: bf16 [num_slots][heads][head_dim][lpad]  (V transposed per head, so
+ *       the P.V contraction streams keys contiguously)
+ * lpad >= the plan's max_slot_len, a multiple of WAVE_KEY_TILE.  Tokens
+ * [len, lpad) of a written slot are zero. */
+typedef struct wave_kv_cache {
+  void* k;
+  void* vt;
+  int32_t num_slots;
+  int32_t heads;
+  int32_t head_dim; /* 64 or 128 */
+  int32_t lpad;
+} wave_kv_cache;
+
+/* Copy the fresh K/V of round `round` into their physical slots and zero
+ * each slot's tail [len, lpad).  k_src, v_src: device [src_rows][heads][head_dim]
+ * of dtype src_dtype (bf16 copied, fp32 rounded to bf16 to nearest even),
+ * token row stride src_row_stride elements (>= heads*head_dim), rows packed in
+ * the round's write order (view.writes[round_write_begin[round] ..]).
+ * d_desc: device copy of this plan's descriptor.  stream: hipStream_t (NULL =
+ * default stream).  Asynchronous; never synchronises.  A round with no writes
+ * is a no-op. */
+int32_t kv_write(const wave_plan_t* plan, const void* d_desc, int32_t round,
+                 const wave_kv_cache* cache, const void* k_src, const void* v_src,
+                 int32_t src_dtype, int64_t src_row_stride, void* stream);
+
+/* Block-causal attention of every node of round `round`.
+ *   q  : device [round_q_rows][heads][head_dim], dtype q_dtype (bf16, or fp32
+ *        rounded to bf16 to nearest even on load), row stride q_row_stride elements.
+ *   o  : device bf16 [round_q_rows][heads][head_dim], dense.
+ *   lse: device fp32 [heads][round_q_rows] natural-log sum of exp of the scaled
+ *        scores, or NULL.
+ * scale multiplies Q.K (typically 1/sqrt(head_dim)).  Softmax in fp32, both
+ * contractions in bf16 with fp32 accumulation.  Each node's result depends on
+ * its query rows and the contents of its gather list only, with a fixed
+ * reduction order, so it is bitwise the same in any schedule.  The plan's
+ * q_tile must be WAVE_Q_TILE.  Asynchronous on `stream`. */
+int32_t wave_attn(const wave_plan_t* plan, const void* d_desc, int32_t round,
+                  const wave_kv_cache* cache, const void* q, int32_t q_dtype,
+                  int64_t q_row_stride, void* o, float* lse, float scale, void* stream);
+
+/* Message of the last failed call on this thread ("" if none).  Valid until
+ * the next call into this library from the same thread. */
+const char* wave_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WAVE_H */

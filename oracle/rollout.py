@@ -25,12 +25,13 @@ from .plan import Params, context
 
 
 def rollout(p: Params, plan: dict, get_q, get_kv, scale: float, rows=None,
-            heads=None, nodes_filter=None):
+            heads=None, want=None):
     """Run `plan` serially; return {(chunk, level): (O [rows, h, dv], LSE [h, rows])}.
 
     rows(chunk, level) -> index array of query rows to compute (default: all).
     heads: iterable of head indices (default: all).
-    nodes_filter(chunk, level) -> bool: compute outputs only for those nodes.
+    want: set of (chunk, level) nodes to compute (default: all); the rollout
+    stops once they are done.
     """
     cache: dict[tuple[int, int], tuple[np.ndarray, np.ndarray]] = {}
     nodes = plan["nodes"]
@@ -53,7 +54,7 @@ def rollout(p: Params, plan: dict, get_q, get_kv, scale: float, rows=None,
             for s in ctx_def:
                 if s not in cache:
                     raise RuntimeError(f"node ({c},{lv}) in round {t} reads unwritten slot {s}")
-            if nodes_filter is None or nodes_filter(c, lv):
+            if want is None or (c, lv) in want:
                 q = np.asarray(get_q(c, lv), np.float64)
                 sel = np.arange(q.shape[0]) if rows is None else np.asarray(rows(c, lv))
                 keys = list(cache.keys())
@@ -73,4 +74,6 @@ def rollout(p: Params, plan: dict, get_q, get_kv, scale: float, rows=None,
                 future_reads[s] -= 1
                 if future_reads[s] == 0:
                     del cache[s]
+        if want is not None and all(k in out for k in want):
+            break
     return out

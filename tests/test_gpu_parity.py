@@ -1,0 +1,217 @@
+"""GPU parity: kv_write and wave_attn (through the C ABI) against the oracle.
+
+Every case prints its name before touching the GPU.  Caches start filled with
+NaN, so a read of an unwritten slot or of a slot outside the gather list
+poisons the output.
+"""
+import numpy as np
+import pytest
+
+import block_causal_attention_wave_amd as wv
+from oracle import plan as op
+from oracle.attention import round_to_bf16
+import wave_inputs as wi
+from gpu_common import (HostInputs, compare, gpu_rollout, log, oracle_rollout, sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("hd", [64, 128])
+@pytest.mark.parametrize("src", ["fp32", "bf16"])
+def test_kv_write_layout(gpu_device, hd, src):
+    import torch
+    log(f"kv_write layout hd={hd} src={src}")
+    B, K, L, Cn, heads = 3, 2, 100, 37, 3
+    plan = wv.wave_plan(B=B, K=K, policy=wv.PROGRESSIVE, sched=wv.WAVE, chunk_len=L, cond_len=Cn)
+    inp = HostInputs(11, heads, hd, L, Cn)
+    desc = plan.upload(gpu_device)
+    cache = wv.KVCache(plan.num_phys_slots, heads, hd, plan.lpad(), gpu_device, fill=float("nan"))
+    dt = torch.float32 if src == "fp32" else torch.bfloat16
+    for t in range(plan.num_rounds):
+        before_k = cache.k.float().cpu().numpy()
+        before_v = cache.vt.float().cpu().numpy()
+        writes = plan.round_writes(t).tolist()
+        ks = [inp.kv(c, lv)[0] for (c, lv, _, _) in writes]
+        vs = [inp.kv(c, lv)[1] for (c, lv, _, _) in writes]
+        k_src = torch.from_numpy(np.concatenate(ks)).to(gpu_device, dt)
+        v_src = torch.from_numpy(np.concatenate(vs)).to(gpu_device, dt)
+        wv.kv_write(plan, desc, t, cache, k_src, v_src)
+        torch.cuda.synchronize()
+        kc = cache.k.float().cpu().numpy()
+        vc = cache.vt.float().cpu().numpy()
+        touched = set()
+        for (c, lv, pid, ln), k, v in zip(writes, ks, vs):
+            touched.add(pid)
+            # torch's float32 -> bfloat16 cast and the kernel's conversion
+            # both round to nearest even, as round_to_bf16 does.
+            kb = round_to_bf16(k)
+            vb = round_to_bf16(v)
+            assert np.array_equal(kc[pid, :, :ln, :], kb.transpose(1, 0, 2)), (t, c, lv)
+            assert np.array_equal(vc[pid, :, :, :ln], vb.transpose(1, 2, 0)), (t, c, lv)
+            assert np.all(kc[pid, :, ln:, :] == 0) and np.all(vc[pid, :, :, ln:] == 0)
+        for pid in range(plan.num_phys_slots):
+            if pid not in touched:
+                assert np.array_equal(np.isnan(kc[pid]), np.isnan(before_k[pid]))
+                assert np.array_equal(np.nan_to_num(kc[pid]), np.nan_to_num(before_k[pid]))
+                assert np.array_equal(np.nan_to_num(vc[pid]), np.nan_to_num(before_v[pid]))
+
+
+def test_tiny_workload_full_rollout(gpu_device):
+    """The tiny workload: every row of every node of the pipelined rollout."""
+    w = wi.WORKLOADS[1]
+    log(f"tiny rollout {w.name}")
+    plan = wv.wave_plan(B=w.B, K=w.K, policy=wi.PROGRESSIVE, sched=wv.WAVE, chunk_len=w.chunk_len)
+    inp = HostInputs(w.key, w.heads, w.head_dim, w.chunk_len, 0)
+    got = gpu_rollout(plan, inp, gpu_device, w.scale, src_dtype="fp32")
+    ref = oracle_rollout(w.B, w.K, wi.PROGRESSIVE, -1, w.chunk_len, 0, inp, w.scale)
+    assert set(got) == set(ref) and len(ref) == 11
+    for key in ref:
+        s = compare(got[key][0], got[key][1], ref[key][0], ref[key][1], f"node {key}")
+    log(f"  last node stats {s}")
+
+
+GRID = [
+    # policy, H, cond, L, heads, hd, dtype
+    (wi.PROGRESSIVE, -1, 0, 300, 2, 128, "bf16"),
+    (wi.SAME_LEVEL, -1, 70, 300, 2, 128, "fp32"),
+    (wi.CLEAN, -1, 0, 129, 3, 64, "bf16"),
+    (wi.PROGRESSIVE, 1, 33, 520, 1, 128, "bf16"),
+    (wi.SAME_LEVEL, 0, 0, 64, 2, 64, "fp32"),
+    (wi.PROGRESSIVE, 2, 1, 1, 2, 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("policy,H,cond,L,heads,hd,dtype", GRID)
+def test_small_grid_parity(gpu_device, policy, H, cond, L, heads, hd, dtype):
+    B, K = 5, 3
+    log(f"grid policy={policy} H={H} cond={cond} L={L} heads={heads} hd={hd} {dtype}")
+    plan = wv.wave_plan(B=B, K=K, policy=policy, sched=wv.WAVE, chunk_len=L, cond_len=cond, history_cap=H)
+    inp = HostInputs(100 + L, heads, hd, L, cond, bf16=(dtype == "bf16"))
+    scale = 1.0 / np.sqrt(hd)
+    got = gpu_rollout(plan, inp, gpu_device, scale, src_dtype=dtype)
+    ref = oracle_rollout(B, K, policy, H, L, cond, inp, scale)
+    assert set(got) == set(ref)
+    for key in ref:
+        compare(got[key][0], got[key][1], ref[key][0], ref[key][1], f"node {key}")
+
+
+@pytest.mark.parametrize("policy", [wi.CLEAN, wi.SAME_LEVEL, wi.PROGRESSIVE])
+def test_serial_and_wave_schedules_bitwise_equal(gpu_device, policy):
+    B, K, L, heads, hd, cond = 5, 3, 200, 2, 128, 40
+    log(f"serial vs wave policy={policy}")
+    inp = HostInputs(7, heads, hd, L, cond)
+    outs = {}
+    for sched in (wv.SERIAL, wv.WAVE):
+        plan = wv.wave_plan(B=B, K=K, policy=policy, sched=sched, chunk_len=L, cond_len=cond)
+        outs[sched] = gpu_rollout(plan, inp, gpu_device, 0.1, src_dtype="fp32")
+    assert set(outs[wv.SERIAL]) == set(outs[wv.WAVE])
+    for key in outs[wv.WAVE]:
+        assert np.array_equal(outs[wv.SERIAL][key][0], outs[wv.WAVE][key][0]), key
+        assert np.array_equal(outs[wv.SERIAL][key][1], outs[wv.WAVE][key][1]), key
+
+
+def test_causality_invariance_and_sensitivity(gpu_device):
+    B, K, L, heads, hd = 6, 2, 150, 2, 128
+    log("causality invariance")
+    plan = wv.wave_plan(B=B, K=K, policy=wv.PROGRESSIVE, sched=wv.WAVE, chunk_len=L)
+    inp = HostInputs(9, heads, hd, L, 0)
+    base = gpu_rollout(plan, inp, gpu_device, 0.09)
+    later = gpu_rollout(plan, inp, gpu_device, 0.09,
+                        perturb=lambda c, lv, k, v: (k + 3.0, v - 2.0) if c > 2 else (k, v))
+    for (c, lv), (o, lse) in base.items():
+        same = np.array_equal(o, later[(c, lv)][0]) and np.array_equal(lse, later[(c, lv)][1])
+        assert same == (c <= 2), (c, lv)
+    # Under progressive history with K=2, later chunks read chunk 0 at level
+    # max(j - r, 0) <= 1, so slot (0, 2) is in U(0, 2)'s gather list only.
+    other = gpu_rollout(plan, inp, gpu_device, 0.09,
+                        perturb=lambda c, lv, k, v: (k * 2.0, v + 1.0) if (c, lv) == (0, 2) else (k, v))
+    for key, (o, lse) in base.items():
+        same = np.array_equal(o, other[key][0])
+        assert same == (key != (0, 2)), key
+
+
+def _device_round(w, policy, layer, t_meas, device, rows_per_node=256, heads=None):
+    """Run a pipelined plan's kv_writes for rounds <= t_meas and the attention of
+    round t_meas with device-generated bf16 inputs; return GPU outputs, the
+    oracle's on sampled rows, and the plan."""
+    import torch
+    plan = wv.wave_plan(B=w.B, K=w.K, policy=policy, sched=wv.WAVE, chunk_len=w.chunk_len,
+                        cond_len=w.cond_len, history_cap=w.history_cap)
+    desc = plan.upload(device)
+    cache = wv.KVCache(plan.num_phys_slots, w.heads, w.head_dim, plan.lpad(), device, fill=float("nan"))
+    dev_cache = {}
+
+    def kv_dev(c, lv):
+        if (c, lv) not in dev_cache:
+            dev_cache[(c, lv)] = (wi.device_tensor(w, layer, c, lv, "k", device, policy),
+                                  wi.device_tensor(w, layer, c, lv, "v", device, policy))
+        return dev_cache[(c, lv)]
+
+    for t in range(t_meas + 1):
+        ws = plan.round_writes(t).tolist()
+        k_src = torch.cat([kv_dev(c, lv)[0] for (c, lv, _, _) in ws])
+        v_src = torch.cat([kv_dev(c, lv)[1] for (c, lv, _, _) in ws])
+        wv.kv_write(plan, desc, t, cache, k_src, v_src)
+    nodes = plan.round_nodes(t_meas).tolist()
+    qs = {(n[0], n[1]): wi.device_tensor(w, layer, n[0], n[1], "q", device, policy) for n in nodes}
+    q = torch.cat([qs[(n[0], n[1])] for n in nodes])
+    o, lse = wv.wave_attn(plan, desc, t_meas, cache, q, w.scale)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    got = {(n[0], n[1]): (o[n[4]:n[4] + n[5]], lse[:, n[4]:n[4] + n[5]]) for n in nodes}
+
+    rows = sample_rows(w.chunk_len, rows_per_node)
+
+    class DevInputs:
+        def q64(self, c, lv):
+            return qs[(c, lv)].float().cpu().numpy().astype(np.float64)
+
+        def kv64(self, c, lv):
+            k, v = kv_dev(c, lv)
+            return k.float().cpu().numpy().astype(np.float64), v.float().cpu().numpy().astype(np.float64)
+
+    want = {(n[0], n[1]) for n in nodes}
+    ref = oracle_rollout(w.B, w.K, policy, w.history_cap, w.chunk_len, w.cond_len, DevInputs(), w.scale,
+                         rows=lambda c, lv: rows, heads=heads, want=want)
+    del dev_cache
+    return got, ref, rows, plan
+
+
+def test_wan13b_steady_round_sampled(gpu_device):
+    """The 832x480 seven-chunk K=4 progressive round 6 at full size, sampled rows."""
+    w = wi.WORKLOADS[2]
+    log(f"{w.name}: GPU round {w.round}, oracle on sampled rows")
+    got, ref, rows, plan = _device_round(w, wi.PROGRESSIVE, 0, w.round, gpu_device)
+    assert len(ref) == 5
+    for key, (o_ref, lse_ref) in ref.items():
+        o, lse = got[key]
+        s = compare(o[rows], lse[:, rows], o_ref, lse_ref, f"node {key}")
+        log(f"  node {key}: {s}")
+
+
+def test_streamer_round_sampled(gpu_device):
+    """The 640x368 Wan-Streamer shape (cond 512, 40 heads) round 7, sampled rows, 8 heads."""
+    w = wi.WORKLOADS[5]
+    log(f"{w.name}: GPU round {w.round}, oracle on sampled rows")
+    heads = list(range(0, 40, 5))
+    got, ref, rows, plan = _device_round(w, wi.SAME_LEVEL, 0, w.round, gpu_device, rows_per_node=192, heads=heads)
+    assert len(ref) == 2
+    for key, (o_ref, lse_ref) in ref.items():
+        o, lse = got[key]
+        s = compare(o[rows][:, heads], lse[heads][:, rows], o_ref[:, heads], lse_ref[heads], f"node {key}")
+        log(f"  node {key}: {s}")
+
+
+def test_long_video_capped_history_sampled(gpu_device):
+    """B=28, K=4, history capped at 6 chunks, sigma 0.5: a steady round."""
+    w = wi.WORKLOADS[4]
+    t = 16
+    log(f"{w.name}: GPU round {t}, oracle on sampled rows, 4 heads")
+    heads = [0, 3, 7, 11]
+    got, ref, rows, plan = _device_round(w, wi.PROGRESSIVE, 0, t, gpu_device, rows_per_node=128, heads=heads)
+    assert len(ref) == 5
+    for key, (o_ref, lse_ref) in ref.items():
+        o, lse = got[key]
+        s = compare(o[rows][:, heads], lse[heads][:, rows], o_ref[:, heads], lse_ref[heads], f"node {key}")
+        log(f"  node {key}: {s}")

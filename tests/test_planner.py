@@ -1,0 +1,183 @@
+"""Native planner (libwave.so, through the C ABI) against the brute-force oracle.
+
+Plans, gather lists, write lists and physical slots must match bit-exactly;
+the work list and the descriptor are checked for their own invariants.
+Runs on the CPU: wave_plan is host code.
+"""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from block_causal_attention_wave_amd import _lib
+import block_causal_attention_wave_amd as wv
+from oracle import plan as op
+from wave_inputs import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def native(B, K, policy, sched, H=-1, L=16, cond=0, q_tile=0):
+    return wv.wave_plan(B=B, K=K, policy=policy, sched=sched, history_cap=H, chunk_len=L,
+                        cond_len=cond, q_tile=q_tile)
+
+
+def assert_same(pn, po):
+    assert pn.num_rounds == po["num_rounds"]
+    assert pn.num_phys_slots == po["num_phys_slots"]
+    assert pn.round_node_begin.tolist() == po["round_node_begin"]
+    assert [tuple(x) for x in pn.nodes.tolist()] == [tuple(x) for x in po["nodes"]]
+    assert [tuple(x) for x in pn.ctx.tolist()] == [tuple(x) for x in po["ctx"]]
+    assert [tuple(x) for x in pn.writes.tolist()] == [tuple(x) for x in po["writes"]]
+
+
+GRID = [(B, K, pol, sch, H, cond)
+        for B in (1, 2, 3, 5, 7, 12)
+        for K in (1, 2, 3, 4, 6)
+        for pol in (op.CLEAN, op.SAME_LEVEL, op.PROGRESSIVE)
+        for sch in (op.SERIAL, op.WAVE)
+        for H in (-1, 0, 1, 2, 6)
+        for cond in (0, 1)]
+
+
+@pytest.mark.parametrize("B,K,pol,sch,H,cond", GRID)
+def test_planner_matches_oracle_grid(B, K, pol, sch, H, cond):
+    L, C_ = 48, (17 if cond else 0)
+    pn = native(B, K, pol, sch, H, L, C_)
+    po = op.oracle_plan(op.Params(B, K, pol, sch, H, L, C_))
+    assert_same(pn, po)
+
+
+@pytest.mark.parametrize("key", sorted(WORKLOADS))
+def test_planner_matches_oracle_workloads(key):
+    w = WORKLOADS[key]
+    for pol in w.policies:
+        for sch in (op.SERIAL, op.WAVE):
+            pn = native(w.B, w.K, pol, sch, w.history_cap, w.chunk_len, w.cond_len)
+            po = op.oracle_plan(op.Params(w.B, w.K, pol, sch, w.history_cap, w.chunk_len, w.cond_len))
+            assert_same(pn, po)
+
+
+def test_workload_capacities_and_rounds():
+    """Round counts and slot capacities of the named workloads."""
+    cases = {
+        (7, 4, op.PROGRESSIVE, -1): (10, 7),
+        (7, 5, op.PROGRESSIVE, -1): (11, 7),
+        (7, 5, op.SAME_LEVEL, -1): (11, 25),
+        (7, 5, op.CLEAN, -1): (35, 7),
+        (28, 4, op.PROGRESSIVE, 6): (31, 11),
+        (4, 2, op.PROGRESSIVE, -1): (5, 4),
+    }
+    for (B, K, pol, H), (R, cap) in cases.items():
+        pn = native(B, K, pol, op.WAVE, H, 4680)
+        assert (pn.num_rounds, pn.num_phys_slots) == (R, cap)
+    pn = native(8, 2, op.SAME_LEVEL, op.WAVE, -1, 2824, 512)
+    assert (pn.num_rounds, pn.num_phys_slots) == (9, 23)
+
+
+def test_work_list_covers_nodes_and_is_sorted():
+    pn = native(7, 4, op.PROGRESSIVE, op.WAVE, -1, 4680, 0)
+    assert pn.q_tile == 256
+    for t in range(pn.num_rounds):
+        items = pn.work[pn.round_work_begin[t]:pn.round_work_begin[t + 1]]
+        nb, ne = pn.round_node_begin[t], pn.round_node_begin[t + 1]
+        cover = {}
+        for node, q0, qr, keys in items.tolist():
+            assert nb <= node < ne
+            n = pn.nodes[node]
+            assert 0 < qr <= 256 and q0 % 256 == 0 and q0 + qr <= n[5]
+            assert keys == int(pn.node_ctx(n)[:, 3].sum())
+            cover.setdefault(node, []).append((q0, qr))
+        for node in range(nb, ne):
+            rows = sorted(cover[node])
+            assert rows[0][0] == 0 and sum(r for _, r in rows) == pn.nodes[node][5]
+        tiles = [int(np.ceil(pn.node_ctx(pn.nodes[it[0]])[:, 3] / 64).sum()) for it in items]
+        assert tiles == sorted(tiles, reverse=True)
+
+
+def test_descriptor_layout():
+    pn = native(5, 3, op.PROGRESSIVE, op.WAVE, 2, 100, 7)
+    d = pn.desc()
+    assert d[0] == 0x57415645 and d[1] == 1
+    nr, nn, nc, nw, nk = d[2:7]
+    assert (nr, nn, nc, nw, nk) == (pn.num_rounds, len(pn.nodes), len(pn.ctx), len(pn.writes), len(pn.work))
+    off_r, off_n, off_c, off_w, off_k = d[7:12]
+    rt = d[off_r:off_r + 8 * nr].reshape(nr, 8)
+    assert rt[:, 0].tolist() == pn.round_node_begin[:-1].tolist()
+    assert rt[:, 6].tolist() == pn.round_q_rows.tolist()
+    assert rt[:, 7].tolist() == pn.round_src_rows.tolist()
+    nt = d[off_n:off_n + 4 * nn].reshape(nn, 4)
+    assert (nt[:, 0] == pn.nodes[:, 4]).all() and (nt[:, 3] == pn.nodes[:, 7]).all()
+    ct = d[off_c:off_c + 2 * nc].reshape(nc, 2)
+    assert (ct[:, 0] == pn.ctx[:, 2]).all() and (ct[:, 1] == pn.ctx[:, 3]).all()
+    wt = d[off_w:off_w + 4 * nw].reshape(nw, 4)
+    for t in range(nr):
+        w0, w1 = pn.round_write_begin[t], pn.round_write_begin[t + 1]
+        assert wt[w0:w1, 2].tolist() == np.concatenate([[0], np.cumsum(pn.writes[w0:w1, 3])[:-1]]).tolist()
+    assert len(d) == off_k + 4 * nk
+    # deterministic
+    assert np.array_equal(d, native(5, 3, op.PROGRESSIVE, op.WAVE, 2, 100, 7).desc())
+
+
+@pytest.mark.parametrize("bad", [
+    dict(B=0), dict(K=0), dict(policy=3), dict(sched=2), dict(history_cap=-2),
+    dict(chunk_len=0), dict(cond_len=-1), dict(q_tile=-1),
+])
+def test_invalid_params_rejected(bad):
+    kw = dict(B=3, K=2, policy=0, sched=1, history_cap=-1, chunk_len=8, cond_len=0, q_tile=0)
+    kw.update(bad)
+    with pytest.raises(wv.WaveError) as e:
+        wv.wave_plan(**kw)
+    assert e.value.code == _lib.WAVE_ERR_INVALID_ARG
+    assert "wave_plan" in str(e.value)
+
+
+def test_abi_exports_every_header_symbol():
+    with open(os.path.join(ROOT, "include", "wave.h")) as f:
+        hdr = f.read()
+    declared = set(re.findall(r"^\s*(?:int32_t|void|const char\*)\s+(\w+)\(", hdr, re.M))
+    assert declared == set(_lib.EXPORTS)
+    lib = C.CDLL(_lib.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_device_calls_validate_before_launch():
+    """Errors that must be caught on the host, before any launch (no GPU needed)."""
+    lib = _lib.load()
+    pn = native(4, 2, op.PROGRESSIVE, op.WAVE, -1, 128, 0)
+    fake = C.c_void_p(0x10000)  # never dereferenced: validation fails first
+    cache = _lib.KvCache(0x10000, 0x20000, 4, 2, 64, 128)
+    stream = C.c_void_p(0)
+
+    def attn(round_=0, cache_=cache, q=fake, qd=0, stride=128, scale=0.125, desc=fake):
+        return lib.wave_attn(pn.handle, desc, round_, C.byref(cache_), q, qd, stride, fake, None,
+                             scale, stream)
+
+    assert attn(round_=5) == _lib.WAVE_ERR_INVALID_ARG
+    assert attn(round_=-1) == _lib.WAVE_ERR_INVALID_ARG
+    assert attn(desc=None) == _lib.WAVE_ERR_INVALID_ARG
+    assert attn(q=None) == _lib.WAVE_ERR_INVALID_ARG
+    assert attn(qd=7) == _lib.WAVE_ERR_UNSUPPORTED
+    assert attn(stride=64) == _lib.WAVE_ERR_INVALID_ARG
+    assert attn(scale=float("nan")) == _lib.WAVE_ERR_INVALID_ARG
+    assert attn(cache_=_lib.KvCache(0x10000, 0x20000, 3, 2, 64, 128)) == _lib.WAVE_ERR_CAPACITY
+    assert attn(cache_=_lib.KvCache(0x10000, 0x20000, 4, 2, 64, 64)) == _lib.WAVE_ERR_CAPACITY
+    assert attn(cache_=_lib.KvCache(0x10000, 0x20000, 4, 2, 96, 128)) == _lib.WAVE_ERR_UNSUPPORTED
+    assert attn(cache_=_lib.KvCache(0x10000, 0x20000, 4, 2, 64, 100)) == _lib.WAVE_ERR_INVALID_ARG
+    assert attn(cache_=_lib.KvCache(0, 0x20000, 4, 2, 64, 128)) == _lib.WAVE_ERR_INVALID_ARG
+    assert b"capacity" in lib.wave_last_error() or len(lib.wave_last_error()) > 0
+    pn128 = native(4, 2, op.PROGRESSIVE, op.WAVE, -1, 128, 0, q_tile=128)
+    assert lib.wave_attn(pn128.handle, fake, 0, C.byref(cache), fake, 0, 128, fake, None, 0.1,
+                         stream) == _lib.WAVE_ERR_UNSUPPORTED
+
+    def kvw(round_=0, src=fake, dt=0, stride=128):
+        return lib.kv_write(pn.handle, fake, round_, C.byref(cache), src, src, dt, stride, stream)
+
+    assert kvw(round_=9) == _lib.WAVE_ERR_INVALID_ARG
+    assert kvw(src=None) == _lib.WAVE_ERR_INVALID_ARG
+    assert kvw(dt=5) == _lib.WAVE_ERR_UNSUPPORTED
+    assert kvw(stride=10) == _lib.WAVE_ERR_INVALID_ARG
+    assert kvw(src=C.c_void_p(0x10008)) == _lib.WAVE_ERR_UNSUPPORTED
