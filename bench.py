@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Benchmark of one pipelined wave round of block-causal attention on one MI355X.
+
+A step is one pass of the round's device path: ``kv_write`` of the round's
+fresh K/V into the cache, then ``wave_attn`` of every query chunk in flight.
+The plan (host) is built once before timing: one plan serves every round and
+every layer of a rollout; its host cost is reported as ``plan_ms``.
+
+Default workload: the Wan2.1-T2V-1.3B 832x480 shape (12 heads x 128, 4680
+tokens per 3-latent-frame chunk, 7 chunks), K=4 levels, progressive history,
+pipelined round 6: R(2), U(3,1), U(4,2), U(5,3), U(6,4) over 32,760 keys.
+
+Prints ONE JSON line on stdout.  Extra flags:
+  --workload {2,4,5}     2 (default), 4 = long video steady round, 5 = Wan-Streamer round
+  --no-cpu-baseline      skip the CPU oracle timing
+  --copy-calibration     also run one 1 GiB device copy (HBM counter calibration)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_flops(plan, t, heads, head_dim, rows_per_node=None):
+    """4 * heads * d * sum over nodes of (query rows x unmasked keys)."""
+    total = 0
+    for n in plan.round_nodes(t):
+        keys = int(plan.node_ctx(n)[:, 3].sum())
+        rows = int(n[5]) if rows_per_node is None else rows_per_node
+        total += rows * keys
+    return 4.0 * heads * head_dim * total
+
+
+def kv_write_bytes(plan, t, heads, head_dim, lpad, src_bytes=2):
+    """Read fresh K and V (len rows) + write K and V^T slots (lpad rows each, tail zeroed)."""
+    b = 0
+    for w in plan.round_writes(t):
+        b += 2 * int(w[3]) * heads * head_dim * src_bytes
+        b += 2 * lpad * heads * head_dim * 2
+    return b
+
+
+HBM_PROFILES = {2: "wave_attn_wan13b_round6_hbm.md", 4: "wave_attn_longvideo_round16_hbm.md",
+                5: "wave_attn_streamer_round7_hbm.md"}
+
+
+def traffic_from_profile(workload):
+    """HBM bytes per wave_attn launch from the committed rocprofv3 counter
+    summary, or None if there is none or the kernel source changed since."""
+    import hashlib
+    name = HBM_PROFILES.get(workload)
+    path = os.path.join(ROOT, "profiles", name) if name else None
+    if not path or not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("#", "|", "`")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    try:
+        h = hashlib.sha256()
+        for src in fields["kernel_sources"].split():
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != fields["kernel_source_sha256"]:
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
+
+
+def sample_rows(L, n, seed=1234):
+    rng = np.random.default_rng(seed)
+    must = set(range(min(8, L))) | set(range(max(0, L - 8), L))
+    rest = [r for r in rng.permutation(L).tolist() if r not in must]
+    return np.asarray(sorted(must | set(rest[:max(0, n - len(must))])))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2, choices=(2, 4, 5))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=128, help="query rows per node for the CPU oracle")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(no collectives, no sharding); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_causal_attention_wave_amd as wv
+    import wave_inputs as wi
+
+    device = torch.device("cuda:0")
+    w = wi.WORKLOADS[args.workload]
+    policy = w.policies[0]
+    t_meas = w.round if w.round >= 0 else 16
+    layer = 0
+
+    t0 = time.perf_counter()
+    plan = wv.wave_plan(B=w.B, K=w.K, policy=policy, sched=wv.WAVE, chunk_len=w.chunk_len,
+                        cond_len=w.cond_len, history_cap=w.history_cap)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    desc = plan.upload(device)
+    lpad = plan.lpad()
+    cache = wv.KVCache(plan.num_phys_slots, w.heads, w.head_dim, lpad, device, fill=float("nan"))
+
+    # Prefill: the earlier rounds' K/V writes (their attention is not needed).
+    def fresh(t):
+        ws = plan.round_writes(t).tolist()
+        ks = [wi.device_tensor(w, layer, c, lv, "k", device, policy) for (c, lv, _, _) in ws]
+        vs = [wi.device_tensor(w, layer, c, lv, "v", device, policy) for (c, lv, _, _) in ws]
+        return torch.cat(ks), torch.cat(vs)
+
+    for t in range(t_meas):
+        k_src, v_src = fresh(t)
+        wv.kv_write(plan, desc, t, cache, k_src, v_src)
+    k_src, v_src = fresh(t_meas)
+    nodes = plan.round_nodes(t_meas).tolist()
+    q = torch.cat([wi.device_tensor(w, layer, n[0], n[1], "q", device, policy) for n in nodes])
+    rows = int(plan.round_q_rows[t_meas])
+    o = torch.empty((rows, w.heads, w.head_dim), dtype=torch.bfloat16, device=device)
+    lse = torch.empty((w.heads, rows), dtype=torch.float32, device=device)
+    torch.cuda.synchronize()
+
+    flops = algorithmic_flops(plan, t_meas, w.heads, w.head_dim)
+    kvw_bytes = kv_write_bytes(plan, t_meas, w.heads, w.head_dim, lpad)
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            wv.kv_write(plan, desc, t_meas, cache, k_src, v_src, stream=stream)
+            wv.wave_attn(plan, desc, t_meas, cache, q, w.scale, o=o, lse=lse, stream=stream)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+                torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for e0, e1, e2 in evs:
+            e0.record(stream)
+            wv.kv_write(plan, desc, t_meas, cache, k_src, v_src, stream=stream)
+            e1.record(stream)
+            wv.wave_attn(plan, desc, t_meas, cache, q, w.scale, o=o, lse=lse, stream=stream)
+            e2.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    kvw_ms = np.array([a.elapsed_time(b) for a, b, _ in evs])
+    attn_ms = np.array([b.elapsed_time(c) for _, b, c in evs])
+    if not torch.isfinite(o.float()).all() or not torch.isfinite(lse).all():
+        eprint("non-finite output: a read outside the written slots")
+        sys.exit(3)
+
+    ms_per_step = wall * 1e3 / args.steps
+    attn_avg = float(attn_ms.mean())
+    achieved = flops / (attn_avg * 1e-3) / 1e12
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    eprint(f"[bench] {w.name}: round {t_meas}, {len(nodes)} nodes, {rows} query rows, "
+           f"{flops / 1e12:.3f} TFLOP")
+    eprint(f"[bench] wave_attn {attn_avg:.3f} ms (p10 {np.percentile(attn_ms, 10):.3f}, "
+           f"p90 {np.percentile(attn_ms, 90):.3f}) = {achieved:.1f} TFLOP/s = "
+           f"{100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak")
+    eprint(f"[bench] kv_write {kvw_ms.mean() * 1e3:.1f} us = {kvw_bytes / (kvw_ms.mean() * 1e-3) / 1e9:.0f} GB/s; "
+           f"step {ms_per_step:.3f} ms wall")
+
+    copy_ms = None
+    if args.copy_calibration:
+        n = 1 << 29  # 1 GiB of bf16
+        src = torch.ones(n, dtype=torch.bfloat16, device=device)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_ms = e0.elapsed_time(e1)
+        eprint(f"[bench] 1 GiB copy {copy_ms:.3f} ms = {2 * (1 << 30) / (copy_ms * 1e-3) / 1e9:.0f} GB/s")
+        del src, dst
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, plan, t_meas, nodes, policy, layer, device, args.cpu_rows)
+
+    out = {
+        "metric": "block-causal attn TFLOP/s (% bf16 MFMA peak) + ms/wave round, 832x480, 7 chunks",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "round": t_meas,
+            "policy": wi.POLICY_NAMES[policy],
+            "chunks": w.B, "levels": w.K, "chunk_tokens": w.chunk_len, "cond_tokens": w.cond_len,
+            "heads": w.heads, "head_dim": w.head_dim, "history_cap": w.history_cap,
+            "nodes_in_round": len(nodes), "query_rows": rows,
+            "algorithmic_tflop": round(flops / 1e12, 4),
+        },
+        "attn_ms": round(attn_avg, 4),
+        "kv_write_ms": round(float(kvw_ms.mean()), 4),
+        "round_ms": round(attn_avg + float(kvw_ms.mean()), 4),
+        "pct_bf16_peak": round(100 * achieved / PEAK_BF16_TFLOPS, 2),
+        "kv_write_gbps": round(kvw_bytes / (kvw_ms.mean() * 1e-3) / 1e9, 1),
+        "plan_ms": round(plan_ms, 3),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_from_profile(args.workload),
+        },
+        "cpu_baseline": cpu,
+    }
+    if copy_ms is not None:
+        out["copy_1gib_ms"] = round(copy_ms, 4)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, plan, t_meas, nodes, policy, layer, device, rows_per_node):
+    """The CPU oracle on a bounded sample of the same round: `rows_per_node`
+    query rows of every node, all heads, fp64 with explicit dense masks."""
+    import torch
+    import wave_inputs as wi
+    from oracle import plan as op
+    from oracle.rollout import rollout
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+
+    p = op.Params(w.B, w.K, policy, op.SERIAL, w.history_cap, w.chunk_len, w.cond_len)
+    oplan = op.oracle_plan(p)
+    want = {(n[0], n[1]) for n in nodes}
+    rows = sample_rows(w.chunk_len, rows_per_node)
+    # Every slot the serial rollout writes until it reaches the wanted nodes:
+    # fetched from the seeded generator before the clock starts.
+    need = set()
+    done = set()
+    for t in range(oplan["num_rounds"]):
+        for nd in oplan["nodes"][oplan["round_node_begin"][t]:oplan["round_node_begin"][t + 1]]:
+            for wr in oplan["writes"][nd[8]:nd[8] + nd[9]]:
+                need.add((wr[0], wr[1]))
+            if (nd[0], nd[1]) in want:
+                done.add((nd[0], nd[1]))
+        if done == want:
+            break
+    kv = {}
+    for (c, lv) in need:
+        k = wi.device_tensor(w, layer, c, lv, "k", device, policy).float().cpu().numpy().astype(np.float64)
+        v = wi.device_tensor(w, layer, c, lv, "v", device, policy).float().cpu().numpy().astype(np.float64)
+        kv[(c, lv)] = (k, v)
+    qs = {(c, lv): wi.device_tensor(w, layer, c, lv, "q", device, policy).float().cpu().numpy().astype(np.float64)
+          for (c, lv) in want}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    out = rollout(p, oplan, lambda c, lv: qs[(c, lv)], lambda c, lv: kv[(c, lv)], w.scale,
+                  rows=lambda c, lv: rows, want=want)
+    secs = time.perf_counter() - t0
+    assert set(out) == want
+    flops = algorithmic_flops(plan, t_meas, w.heads, w.head_dim, rows_per_node=len(rows))
+    eprint(f"[bench] cpu oracle: {len(rows)} rows x {len(nodes)} nodes x {w.heads} heads in {secs:.1f} s "
+           f"({threads} threads) = {flops / secs / 1e9:.2f} GFLOP/s")
+    return {
+        "value": round(flops / secs / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{len(rows)} query rows of each of the {len(nodes)} nodes of round {t_meas}, "
+                  f"all {w.heads} heads, fp64 dense-mask attention over every live slot; "
+                  f"{secs:.1f} s wall; full-round estimate {secs * w.chunk_len / len(rows):.0f} s",
+    }
+
+
+if __name__ == "__main__":
+    main()
