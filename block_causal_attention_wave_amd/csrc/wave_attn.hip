@@ -10,9 +10,9 @@
 // masking left is the ragged tail of a slot's last tile.
 //
 // Work decomposition: one workgroup = 256 query rows of one node and one
-// head; 4 waves, one per SIMD, 64 query rows each.  Key tiles of 64 keys
-// stream through a 3-stage LDS ring filled by direct global->LDS 16-byte
-// loads.
+// head; W waves of 32*QB query rows each.  Key tiles of 64 keys stream through
+// a 4-stage LDS ring filled by direct global->LDS 16-byte loads issued by all
+// waves; one barrier per tile.
 //
 // Contraction layout (bf16 MFMA 32x32x16, fp32 accumulation):
 //   S^T[key][query] = K . Q^T   A = K rows from LDS, B = Q from registers.
@@ -22,8 +22,13 @@
 //     that a lane's 16 accumulator registers are 16 consecutive keys.
 //   O^T[d][query] += V^T . P^T  A = V^T rows from LDS, B = P straight from the
 //     softmax registers (bf16), no data movement.
-// Online softmax in fp32 with exp2 and the scale folded into one FMA
-// (FlashAttention-2 style deferred 1/l normalisation).
+// Online softmax in fp32: exp2 with the scale folded into one FMA, deferred
+// 1/l normalisation (FlashAttention-2), and a lazily raised reference: the
+// row max is only moved (rescaling O and l) when a block's scores exceed it
+// by more than 2^8, so the common block does no O rescale at all.
+// Scores of the next 32-key block are computed while the current block's
+// probabilities are formed, so MFMA and VALU work of one wave can overlap;
+// with two waves per SIMD the hardware interleaves them as well.
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"
@@ -35,24 +40,29 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kThreads = 256;
-constexpr int kKT = 64;     // keys per tile
-constexpr int kStages = 3;  // LDS ring depth
-constexpr int kMaxCtx = 512; // gather-list entries staged in LDS
+constexpr int kKT = 64;       // keys per LDS tile
+constexpr int kStages = 4;    // LDS ring depth
+constexpr int kMaxCtx = 512;  // gather-list entries staged in LDS
+constexpr int kQTile = 256;   // query rows per workgroup
 
-template <int HD>
+// W waves, QB 32-query blocks per wave, head dim HD.
+template <int HD, int W, int QB>
 struct Cfg {
-  static constexpr int KROW = HD * 2;     // bytes per K row in LDS
+  static constexpr int THREADS = 64 * W;
+  static constexpr int KROW = HD * 2;  // bytes per K row in LDS
   static constexpr int KBYTES = kKT * KROW;
-  static constexpr int VROW = kKT * 2;    // bytes per V^T row in LDS
+  static constexpr int VROW = kKT * 2;  // bytes per V^T row in LDS
   static constexpr int VBYTES = HD * VROW;
   static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int NC = HD / 16;      // k-steps of Q.K^T
-  static constexpr int ND = HD / 32;      // d blocks of O^T
-  static constexpr int KLOADS = KBYTES / (kThreads * 16);
-  static constexpr int VLOADS = VBYTES / (kThreads * 16);
+  static constexpr int NC = HD / 16;  // k-steps of Q.K^T
+  static constexpr int ND = HD / 32;  // d blocks of O^T
+  static constexpr int KLOADS = KBYTES / (THREADS * 16);
+  static constexpr int VLOADS = VBYTES / (THREADS * 16);
   static constexpr int LOADS = KLOADS + VLOADS;
+  static_assert(W * 32 * QB == kQTile, "a workgroup covers one query tile");
+  static_assert(KLOADS >= 1 && VLOADS >= 1, "every thread loads part of each tile");
 };
 
 // 16-byte chunk swizzles inside an LDS row: an MFMA operand read has 8 (16)
@@ -74,39 +84,172 @@ __device__ __forceinline__ int perm_key(int i) {
   return kb * 32 + ((ip >> 2) & 1) * 16 + (ip >> 3) * 4 + (ip & 3);
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
+// Per-lane byte offsets of one thread's share of a K/V tile load, relative
+// to the tile's first key in the slot (the wave-uniform part of the address).
+template <int HD, int W, int QB>
+struct TileOffsets {
+  using C = Cfg<HD, W, QB>;
+  uint32_t k[C::KLOADS];
+  uint32_t v[C::VLOADS];
 
-template <int HD>
-__device__ __forceinline__ void issue_tile(char* stage, const __bf16* kslot, const __bf16* vtslot,
-                                           int key0, int lpad, int wv, int lane) {
-  using C = Cfg<HD>;
+  __device__ __forceinline__ TileOffsets(int lpad, int wv, int lane) {
 #pragma unroll
-  for (int n = 0; n < C::KLOADS; ++n) {
-    const int chunk_base = (wv * C::KLOADS + n) * 1024;
-    const int off = chunk_base + lane * 16;
-    const int row = off / C::KROW;
-    const int pc = (off % C::KROW) / 16;
-    const int lc = pc ^ swzK<HD>(row);
-    const __bf16* g = kslot + (int64_t)(key0 + perm_key(row)) * HD + lc * 8;
-    __builtin_amdgcn_global_load_lds(g, (lds_void*)(stage + chunk_base), 16, 0, 0);
+    for (int n = 0; n < C::KLOADS; ++n) {
+      const int off = (wv * C::KLOADS + n) * 1024 + lane * 16;
+      const int row = off / C::KROW;
+      const int lc = ((off % C::KROW) / 16) ^ swzK<HD>(row);
+      k[n] = (uint32_t)((perm_key(row) * HD + lc * 8) * 2);
+    }
+#pragma unroll
+    for (int n = 0; n < C::VLOADS; ++n) {
+      const int off = (wv * C::VLOADS + n) * 1024 + lane * 16;
+      const int d = off / C::VROW;
+      const int lc = ((off % C::VROW) / 16) ^ swz8(d);
+      v[n] = (uint32_t)((d * lpad + lc * 8) * 2);
+    }
   }
+};
+
+// Issue one thread's direct global->LDS loads of a 64-key K tile (rows
+// permuted, chunks swizzled) and the matching V^T tile.  kt / vt point at the
+// tile's first key of the slot.
+template <int HD, int W, int QB>
+__device__ __forceinline__ void issue_tile(char* stage, const char* kt, const char* vt,
+                                           const TileOffsets<HD, W, QB>& off, int wv) {
+  using C = Cfg<HD, W, QB>;
 #pragma unroll
-  for (int n = 0; n < C::VLOADS; ++n) {
-    const int chunk_base = (wv * C::VLOADS + n) * 1024;
-    const int off = chunk_base + lane * 16;
-    const int d = off / C::VROW;
-    const int pc = (off % C::VROW) / 16;
-    const int lc = pc ^ swz8(d);
-    const __bf16* g = vtslot + (int64_t)d * lpad + key0 + lc * 8;
-    __builtin_amdgcn_global_load_lds(g, (lds_void*)(stage + C::KBYTES + chunk_base), 16, 0, 0);
+  for (int n = 0; n < C::KLOADS; ++n)
+    __builtin_amdgcn_global_load_lds(kt + off.k[n], (lds_void*)(stage + (wv * C::KLOADS + n) * 1024), 16, 0, 0);
+#pragma unroll
+  for (int n = 0; n < C::VLOADS; ++n)
+    __builtin_amdgcn_global_load_lds(vt + off.v[n], (lds_void*)(stage + C::KBYTES + (wv * C::VLOADS + n) * 1024),
+                                     16, 0, 0);
+}
+
+// Row max / sum across the two half-waves (lanes l and l^32 hold the same query).
+__device__ __forceinline__ float halfwave_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float halfwave_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Raw scores of one 32-key block (kb = 0 or 1 of a 64-key LDS tile) against
+// the wave's 32*QB queries, as S^T blocks s[qb] (32 keys x 32 queries).
+template <int HD, int QB>
+__device__ __forceinline__ void qk_block(const char* ks, int kb, const bf16x8 (&qop)[QB][HD / 16],
+                                         f32x16 (&s)[QB], int lane) {
+  const int row = kb * 32 + (lane & 31);
+  const char* rp = ks + row * (HD * 2);
+  const int sw = swzK<HD>(row);
+#pragma unroll
+  for (int cc = 0; cc < HD / 16; ++cc) {
+    const bf16x8 av = *reinterpret_cast<const bf16x8*>(rp + (((2 * cc + (lane >> 5)) ^ sw) * 16));
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qop[qb][cc], cc == 0 ? f32x16{} : s[qb], 0, 0, 0);
   }
 }
 
-template <int HD>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+// Keys at or beyond `valid` (counted from the block's first key) get -inf.
+template <int QB>
+__device__ __forceinline__ void mask_block(f32x16 (&s)[QB], int valid, int lane) {
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if ((lane >> 5) * 16 + r >= valid) s[qb][r] = -INFINITY;
+}
+
+__device__ __forceinline__ float block_rowmax(const f32x16& s) {
+  float m0 = fmaxf(s[0], s[1]), m1 = fmaxf(s[2], s[3]);
+#pragma unroll
+  for (int r = 4; r < 16; r += 4) {
+    m0 = fmaxf(m0, fmaxf(s[r], s[r + 1]));
+    m1 = fmaxf(m1, fmaxf(s[r + 2], s[r + 3]));
+  }
+  return halfwave_max(fmaxf(m0, m1));
+}
+
+// p = exp2(s * c2 - mref) (scores to log2 units and the softmax reference in
+// one FMA), packed to bf16 MFMA B operands; the row sums accumulate the fp32
+// probabilities (summing the bf16-rounded ones would cost the LSE up to 2^-9
+// relative on short rows).
+template <int QB>
+__device__ __forceinline__ void softmax_block(const f32x16 (&s)[QB], float c2, const float (&mref)[QB],
+                                              bf16x8 (&pop)[QB][2], float (&l)[QB]) {
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      bf16x8 pv;
+      float sum0 = 0.0f, sum1 = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 8; t += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][8 * hh + t], c2, -mref[qb]));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][8 * hh + t + 1], c2, -mref[qb]));
+        sum0 += p0;
+        sum1 += p1;
+        pv[t] = (__bf16)p0;
+        pv[t + 1] = (__bf16)p1;
+      }
+      l[qb] += sum0 + sum1;
+      pop[qb][hh] = pv;
+    }
+}
+
+// O^T += V^T(block kb) . P^T
+template <int HD, int QB>
+__device__ __forceinline__ void pv_block(const char* vs, int kb, const bf16x8 (&pop)[QB][2],
+                                         f32x16 (&o)[HD / 32][QB], int lane) {
+#pragma unroll
+  for (int db = 0; db < HD / 32; ++db) {
+    const int d = db * 32 + (lane & 31);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int kc = 4 * kb + 2 * (lane >> 5) + hh;
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(vs + d * (kKT * 2) + ((kc ^ swz8(d)) * 16));
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pop[qb][hh], o[db][qb], 0, 0, 0);
+    }
+  }
+}
+
+// A block whose scores exceed the softmax reference by more than this many
+// powers of two raises the reference (rescaling O and l); below that the
+// stale reference is kept: p <= 2^8 is exact enough in fp32 and bf16.
+constexpr float kRescaleLog2 = 8.0f;
+
+// Walks the gather list tile by tile.
+struct Walker {
+  const int* ctx;
+  int e = 0, t = 0;
+  // Values read from LDS are per-lane to the compiler; they are the same in
+  // every lane, and saying so keeps addresses and loop bounds in SGPRs.
+  __device__ __forceinline__ int phys() const { return __builtin_amdgcn_readfirstlane(ctx[2 * e]); }
+  __device__ __forceinline__ int len() const { return __builtin_amdgcn_readfirstlane(ctx[2 * e + 1]); }
+  __device__ __forceinline__ int key0() const { return t * kKT; }
+  __device__ __forceinline__ int valid() const { return len() - t * kKT; }  // >= kKT: full tile
+  __device__ __forceinline__ void next() {
+    if ((t + 1) * kKT >= len()) {
+      ++e;
+      t = 0;
+    } else {
+      ++t;
+    }
+  }
+};
+
+template <int HD, int W, int QB>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * W, 64 * W), amdgpu_waves_per_eu(W / 4, W / 4)))
 void wave_attn_kernel(AttnArgs a) {
-  using C = Cfg<HD>;
-  __shared__ __attribute__((aligned(1024))) char lds[kStages * C::STAGE];
+  using C = Cfg<HD, W, QB>;
+  constexpr int NS = kStages;
+  __shared__ __attribute__((aligned(1024))) char lds[NS * C::STAGE];
   __shared__ int ctx_lds[2 * kMaxCtx];
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -123,18 +266,19 @@ void wave_attn_kernel(AttnArgs a) {
 
   // The gather list goes to LDS once, so that walking it inside the tile
   // loop never waits on the vector-memory counter the K/V prefetch uses.
-  for (int e = threadIdx.x; e < 2 * ctx_count; e += kThreads) ctx_lds[e] = ctx_g[e];
+  for (int e = threadIdx.x; e < 2 * ctx_count; e += C::THREADS) ctx_lds[e] = ctx_g[e];
   __syncthreads();
-  const int* ctx = ctx_lds;
   int total_tiles = 0;
-  for (int e = 0; e < ctx_count; ++e) total_tiles += (ctx[2 * e + 1] + kKT - 1) / kKT;
+  for (int e = 0; e < ctx_count; ++e) total_tiles += (ctx_lds[2 * e + 1] + kKT - 1) / kKT;
+  total_tiles = __builtin_amdgcn_readfirstlane(total_tiles);
 
   // Q fragments (B operand of S^T): lane holds query (lane & 31) of block qb,
   // dims 16c + 8*(lane>>5) .. +7.
-  bf16x8 qop[2][C::NC];
+  const float c2 = a.scale_log2e;
+  bf16x8 qop[QB][C::NC];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int r = wv * 64 + qb * 32 + (lane & 31);
+  for (int qb = 0; qb < QB; ++qb) {
+    const int r = (wv * QB + qb) * 32 + (lane & 31);
     const bool valid = r < q_rows;
     const int64_t base = (int64_t)(q_offset + q_start + r) * a.q_row_stride + (int64_t)h * HD + 8 * (lane >> 5);
 #pragma unroll
@@ -144,9 +288,11 @@ void wave_attn_kernel(AttnArgs a) {
         for (int i = 0; i < 8; ++i) v[i] = (__bf16)0.0f;
       } else if (a.q_fp32) {
         const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(a.q) + base + 16 * c);
-        const f32x4 x = p[0], y = p[1];
-        v[0] = (__bf16)x[0]; v[1] = (__bf16)x[1]; v[2] = (__bf16)x[2]; v[3] = (__bf16)x[3];
-        v[4] = (__bf16)y[0]; v[5] = (__bf16)y[1]; v[6] = (__bf16)y[2]; v[7] = (__bf16)y[3];
+        const f32x4 u = p[0], w = p[1];
+        for (int i = 0; i < 4; ++i) {
+          v[i] = (__bf16)u[i];
+          v[4 + i] = (__bf16)w[i];
+        }
       } else {
         v = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.q) + base + 16 * c);
       }
@@ -154,150 +300,119 @@ void wave_attn_kernel(AttnArgs a) {
     }
   }
 
-  f32x16 o[C::ND][2];
+  f32x16 o[C::ND][QB];
 #pragma unroll
   for (int db = 0; db < C::ND; ++db)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[db][qb][i] = 0.0f;
-  float m[2] = {-INFINITY, -INFINITY};
-  float l[2] = {0.0f, 0.0f};
-  const float c2 = a.scale_log2e;
-
-  // Load iterator.
-  int le = 0, lt = 0;
-  auto next_load = [&](int stage) {
-    const int phys = ctx[2 * le];
-    const int len = ctx[2 * le + 1];
-    issue_tile<HD>(lds + stage * C::STAGE, kcache + phys * slot_elems, vcache + phys * slot_elems,
-                   lt * kKT, lpad, wv, lane);
-    if ((lt + 1) * kKT >= len) {
-      ++le;
-      lt = 0;
-    } else {
-      ++lt;
-    }
-  };
+  // Softmax reference per query in log2 units (c2 * a raw score): exact row
+  // max of the first block, raised lazily afterwards.
+  float mref[QB], l[QB];
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < total_tiles) next_load(s);
+  for (int qb = 0; qb < QB; ++qb) l[qb] = 0.0f;
 
-  int ce = 0, ct = 0;  // compute iterator
-  for (int n = 0; n < total_tiles; ++n) {
-    if (n + 1 < total_tiles) {
-      // tile n+1 may still be in flight
-      __builtin_amdgcn_s_waitcnt((C::LOADS & 15) | ((C::LOADS >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-    } else {
-      __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
-    }
-    // Raw barrier: the counters above already cover this thread's LDS fills,
-    // and every wave finished reading the stage about to be refilled.
+  Walker ld{ctx_lds};
+  const TileOffsets<HD, W, QB> toff(lpad, wv, lane);
+  auto issue = [&](int stage) {
+    const int64_t slot = (int64_t)ld.phys() * slot_elems;
+    const char* kt = reinterpret_cast<const char*>(kcache + slot + (int64_t)ld.key0() * HD);
+    const char* vt = reinterpret_cast<const char*>(vcache + slot + ld.key0());
+    issue_tile<HD, W, QB>(lds + stage * C::STAGE, kt, vt, toff, wv);
+    ld.next();
+  };
+  constexpr int kWaitExp = (0x7 << 4) | (0xF << 8);
+  auto wait_tiles = [&](int later) {  // wait until at most `later` tiles of loads are in flight
+    if (later >= 2) __builtin_amdgcn_s_waitcnt(kWaitExp | ((2 * C::LOADS) & 15) | (((2 * C::LOADS) >> 4) << 14));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(kWaitExp | (C::LOADS & 15) | ((C::LOADS >> 4) << 14));
+    else __builtin_amdgcn_s_waitcnt(kWaitExp);
+  };
+  // Raw barrier: the wait above covers this thread's LDS fills, and the
+  // compiler barriers keep LDS reads on their side of it.
+  auto barrier = [&]() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (n + kStages - 1 < total_tiles) next_load((n + kStages - 1) % kStages);
+  };
 
-    const char* ks = lds + (n % kStages) * C::STAGE;
-    const char* vs = ks + C::KBYTES;
-    const int len = ctx[2 * ce + 1];
-    const int key0 = ct * kKT;
+  // Prologue: tiles 0..NS-2 in flight; scores of block 0 with an exact row max.
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < total_tiles) issue(s);
+  wait_tiles(min(total_tiles - 1, NS - 2));
+  barrier();
+  Walker cur{ctx_lds};
+  f32x16 sa[QB], sb[QB];
+  qk_block<HD, QB>(lds, 0, qop, sa, lane);
+  if (cur.valid() < 32) mask_block<QB>(sa, cur.valid(), lane);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) mref[qb] = c2 * block_rowmax(sa[qb]);
 
-    f32x16 s[2][2];
+  // Raise the reference if the freshly computed block exceeds it by more
+  // than 2^kRescaleLog2 (wave-uniform branch; rare after the first blocks).
+  auto check = [&](const f32x16 (&snew)[QB]) {
+    float over[QB];
+    bool raise = false;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
+      over[qb] = c2 * block_rowmax(snew[qb]) - mref[qb];
+      raise |= over[qb] > kRescaleLog2;
+    }
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < QB; ++qb) {
+        const float delta = fmaxf(over[qb], 0.0f);
+        const float alpha = __builtin_amdgcn_exp2f(-delta);
+        mref[qb] += delta;
+        l[qb] *= alpha;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][qb][i] = 0.0f;
+        for (int db = 0; db < C::ND; ++db)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int row = kb * 32 + (lane & 31);
-#pragma unroll
-      for (int c = 0; c < C::NC; ++c) {
-        const int ch = 2 * c + (lane >> 5);
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(ks + row * C::KROW + ((ch ^ swzK<HD>(row)) * 16));
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qop[qb][c], s[kb][qb], 0, 0, 0);
+          for (int i = 0; i < 16; ++i) o[db][qb][i] *= alpha;
       }
     }
-    if (key0 + kKT > len) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (key0 + kb * 32 + (lane >> 5) * 16 + r >= len) s[kb][qb][r] = -INFINITY;
-    }
+  };
 
-    bf16x8 pop[2][2][2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[qb], mx);
-      const float alpha = __builtin_amdgcn_exp2f((m[qb] - mnew) * c2);
-      m[qb] = mnew;
-      l[qb] *= alpha;
-#pragma unroll
-      for (int db = 0; db < C::ND; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][qb][i] *= alpha;
-      const float nm = -mnew * c2;
-      float sum = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          bf16x8 pv;
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][8 * hh + t], c2, nm));
-            sum += p;
-            pv[t] = (__bf16)p;
-          }
-          pop[kb][qb][hh] = pv;
-        }
-      l[qb] += sum;
+  for (int n = 0; n < total_tiles; ++n) {
+    const char* st = lds + (n % NS) * C::STAGE;
+    const int valid = cur.valid();
+    // Block 0 of tile n (scores in sa) -> scores of block 1 into sb.
+    {
+      bf16x8 pop[QB][2];
+      qk_block<HD, QB>(st, 1, qop, sb, lane);
+      softmax_block<QB>(sa, c2, mref, pop, l);
+      pv_block<HD, QB>(st + C::KBYTES, 0, pop, o, lane);
+      if (valid < 64) mask_block<QB>(sb, valid - 32, lane);
+      check(sb);
     }
-
-#pragma unroll
-    for (int db = 0; db < C::ND; ++db) {
-      const int d = db * 32 + (lane & 31);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int kc = 4 * kb + 2 * (lane >> 5) + hh;
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(vs + d * C::VROW + ((kc ^ swz8(d)) * 16));
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pop[kb][qb][hh], o[db][qb], 0, 0, 0);
-        }
-    }
-
-    if ((ct + 1) * kKT >= len) {
-      ++ce;
-      ct = 0;
-    } else {
-      ++ct;
+    // Block 1 of tile n (scores in sb) -> scores of block 0 of tile n+1 into sa.
+    {
+      bf16x8 pop[QB][2];
+      const bool has_next = n + 1 < total_tiles;
+      if (has_next) {
+        wait_tiles(min(total_tiles - 2 - n, NS - 3));
+        barrier();
+        if (n + NS - 1 < total_tiles) issue((n + NS - 1) % NS);
+        qk_block<HD, QB>(lds + ((n + 1) % NS) * C::STAGE, 0, qop, sa, lane);
+      }
+      softmax_block<QB>(sb, c2, mref, pop, l);
+      pv_block<HD, QB>(st + C::KBYTES, 1, pop, o, lane);
+      cur.next();
+      if (has_next) {
+        if (cur.valid() < 32) mask_block<QB>(sa, cur.valid(), lane);
+        check(sa);
+      }
     }
   }
 
-  // Epilogue: O = O^T / l, LSE = ln2 * (m * c2 + log2 l).
+  // Epilogue: O = O^T / l, LSE = ln2 * (mref + log2 l).
   __bf16* out = static_cast<__bf16*>(a.o);
   const int64_t orow_stride = (int64_t)a.heads * HD;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float ltot = l[qb] + __shfl_xor(l[qb], 32);
+  for (int qb = 0; qb < QB; ++qb) {
+    const float ltot = halfwave_sum(l[qb]);
     const float inv = 1.0f / ltot;
-    const int r = wv * 64 + qb * 32 + (lane & 31);
+    const int r = (wv * QB + qb) * 32 + (lane & 31);
     if (r < q_rows) {
       const int64_t grow = q_offset + q_start + r;
       __bf16* orow = out + grow * orow_stride + (int64_t)h * HD;
@@ -311,19 +426,25 @@ void wave_attn_kernel(AttnArgs a) {
           *reinterpret_cast<bf16x4*>(orow + db * 32 + g * 8 + (lane >> 5) * 4) = v;
         }
       if (a.lse != nullptr && lane < 32)
-        a.lse[(int64_t)h * a.lse_stride + grow] = (m[qb] * c2 + __log2f(ltot)) * 0.69314718055994531f;
+        a.lse[(int64_t)h * a.lse_stride + grow] = (mref[qb] + __log2f(ltot)) * 0.69314718055994531f;
     }
   }
 }
+
+#ifndef WAVE_ATTN_WAVES
+#define WAVE_ATTN_WAVES 8
+#endif
+constexpr int kWaves = WAVE_ATTN_WAVES;
+constexpr int kQB = kQTile / (32 * kWaves);
 
 }  // namespace
 
 hipError_t launch_wave_attn(const AttnArgs& a, hipStream_t stream) {
   if (a.num_work == 0) return hipSuccess;
   dim3 grid(a.num_work * a.heads);
-  dim3 block(kThreads);
-  if (a.head_dim == 128) hipLaunchKernelGGL((wave_attn_kernel<128>), grid, block, 0, stream, a);
-  else hipLaunchKernelGGL((wave_attn_kernel<64>), grid, block, 0, stream, a);
+  dim3 block(64 * kWaves);
+  if (a.head_dim == 128) hipLaunchKernelGGL((wave_attn_kernel<128, kWaves, kQB>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((wave_attn_kernel<64, kWaves, kQB>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
