@@ -110,26 +110,44 @@ struct TileOffsets {
   }
 };
 
+// One 16-byte-per-lane direct global->LDS load: lane i's 16 bytes at
+// base + off land at LDS address lds_addr + 16*i.  Written as inline asm so
+// that the compiler does not treat the asynchronous LDS write as aliasing the
+// ring stages being read (it would then wait for every in-flight tile before
+// each LDS read); completion is tracked explicitly with s_waitcnt vmcnt and
+// the tile barrier.  The instruction has no register results.  M0 is set here
+// and used by nothing else in this kernel.
+__device__ __forceinline__ void load_lds16(uint32_t lds_addr, const char* base, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_addr), "v"(off), "s"(base)
+               : "memory", "m0");
+}
+
 // Issue one thread's direct global->LDS loads of a 64-key K tile (rows
 // permuted, chunks swizzled) and the matching V^T tile.  kt / vt point at the
-// tile's first key of the slot.
+// tile's first key of the slot; wv is the (wave-uniform) wave index.
 template <int HD, int W, int QB>
 __device__ __forceinline__ void issue_tile(char* stage, const char* kt, const char* vt,
                                            const TileOffsets<HD, W, QB>& off, int wv) {
   using C = Cfg<HD, W, QB>;
+  const uint32_t sbase = (uint32_t)(uintptr_t)stage;
 #pragma unroll
   for (int n = 0; n < C::KLOADS; ++n)
-    __builtin_amdgcn_global_load_lds(kt + off.k[n], (lds_void*)(stage + (wv * C::KLOADS + n) * 1024), 16, 0, 0);
+    load_lds16(sbase + (wv * C::KLOADS + n) * 1024, kt, off.k[n]);
 #pragma unroll
   for (int n = 0; n < C::VLOADS; ++n)
-    __builtin_amdgcn_global_load_lds(vt + off.v[n], (lds_void*)(stage + C::KBYTES + (wv * C::VLOADS + n) * 1024),
-                                     16, 0, 0);
+    load_lds16(sbase + C::KBYTES + (wv * C::VLOADS + n) * 1024, vt, off.v[n]);
 }
 
 // Row max / sum across the two half-waves (lanes l and l^32 hold the same query).
+// The max helpers use the NaN-propagating IEEE maximum, which needs no
+// quieting of its inputs (fmaxf does, at one extra instruction per element).
+__device__ __forceinline__ float fmax_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ float halfwave_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmax_nan(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float halfwave_sum(float x) {
@@ -165,13 +183,16 @@ __device__ __forceinline__ void mask_block(f32x16 (&s)[QB], int valid, int lane)
 }
 
 __device__ __forceinline__ float block_rowmax(const f32x16& s) {
-  float m0 = fmaxf(s[0], s[1]), m1 = fmaxf(s[2], s[3]);
+  // two independent chains of 3-input maxima
+  float m0 = fmax_nan(fmax_nan(s[0], s[1]), s[2]);
+  float m1 = fmax_nan(fmax_nan(s[3], s[4]), s[5]);
 #pragma unroll
-  for (int r = 4; r < 16; r += 4) {
-    m0 = fmaxf(m0, fmaxf(s[r], s[r + 1]));
-    m1 = fmaxf(m1, fmaxf(s[r + 2], s[r + 3]));
+  for (int r = 6; r < 14; r += 4) {
+    m0 = fmax_nan(fmax_nan(m0, s[r]), s[r + 1]);
+    m1 = fmax_nan(fmax_nan(m1, s[r + 2]), s[r + 3]);
   }
-  return halfwave_max(fmaxf(m0, m1));
+  m0 = fmax_nan(fmax_nan(m0, s[14]), s[15]);
+  return halfwave_max(fmax_nan(m0, m1));
 }
 
 // p = exp2(s * c2 - mref) (scores to log2 units and the softmax reference in
@@ -224,20 +245,29 @@ __device__ __forceinline__ void pv_block(const char* vs, int kb, const bf16x8 (&
 // stale reference is kept: p <= 2^8 is exact enough in fp32 and bf16.
 constexpr float kRescaleLog2 = 8.0f;
 
-// Walks the gather list tile by tile.
+// Walks the gather list tile by tile, keeping the current slot's index and
+// length in scalar registers.
 struct Walker {
   const int* ctx;
-  int e = 0, t = 0;
+  int count;
+  int e = 0, t = 0, phys_ = 0, len_ = 0;
+  __device__ __forceinline__ Walker(const int* c, int n) : ctx(c), count(n) { load(); }
   // Values read from LDS are per-lane to the compiler; they are the same in
   // every lane, and saying so keeps addresses and loop bounds in SGPRs.
-  __device__ __forceinline__ int phys() const { return __builtin_amdgcn_readfirstlane(ctx[2 * e]); }
-  __device__ __forceinline__ int len() const { return __builtin_amdgcn_readfirstlane(ctx[2 * e + 1]); }
+  __device__ __forceinline__ void load() {
+    if (e < count) {
+      phys_ = __builtin_amdgcn_readfirstlane(ctx[2 * e]);
+      len_ = __builtin_amdgcn_readfirstlane(ctx[2 * e + 1]);
+    }
+  }
+  __device__ __forceinline__ int phys() const { return phys_; }
   __device__ __forceinline__ int key0() const { return t * kKT; }
-  __device__ __forceinline__ int valid() const { return len() - t * kKT; }  // >= kKT: full tile
+  __device__ __forceinline__ int valid() const { return len_ - t * kKT; }  // >= kKT: full tile
   __device__ __forceinline__ void next() {
-    if ((t + 1) * kKT >= len()) {
+    if ((t + 1) * kKT >= len_) {
       ++e;
       t = 0;
+      load();
     } else {
       ++t;
     }
@@ -253,6 +283,7 @@ void wave_attn_kernel(AttnArgs a) {
   __shared__ int ctx_lds[2 * kMaxCtx];
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int wv_u = __builtin_amdgcn_readfirstlane(wv);
   const int item = blockIdx.x / a.heads, h = blockIdx.x % a.heads;
   const int32_t* wk = a.work + 4 * (a.work_begin + item);
   const int node = wk[0], q_start = wk[1], q_rows = wk[2];
@@ -313,13 +344,13 @@ void wave_attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) l[qb] = 0.0f;
 
-  Walker ld{ctx_lds};
+  Walker ld(ctx_lds, ctx_count);
   const TileOffsets<HD, W, QB> toff(lpad, wv, lane);
   auto issue = [&](int stage) {
     const int64_t slot = (int64_t)ld.phys() * slot_elems;
     const char* kt = reinterpret_cast<const char*>(kcache + slot + (int64_t)ld.key0() * HD);
     const char* vt = reinterpret_cast<const char*>(vcache + slot + ld.key0());
-    issue_tile<HD, W, QB>(lds + stage * C::STAGE, kt, vt, toff, wv);
+    issue_tile<HD, W, QB>(lds + stage * C::STAGE, kt, vt, toff, wv_u);
     ld.next();
   };
   constexpr int kWaitExp = (0x7 << 4) | (0xF << 8);
@@ -341,7 +372,7 @@ void wave_attn_kernel(AttnArgs a) {
     if (s < total_tiles) issue(s);
   wait_tiles(min(total_tiles - 1, NS - 2));
   barrier();
-  Walker cur{ctx_lds};
+  Walker cur(ctx_lds, ctx_count);
   f32x16 sa[QB], sb[QB];
   qk_block<HD, QB>(lds, 0, qop, sa, lane);
   if (cur.valid() < 32) mask_block<QB>(sa, cur.valid(), lane);
@@ -373,10 +404,12 @@ void wave_attn_kernel(AttnArgs a) {
     }
   };
 
-  for (int n = 0; n < total_tiles; ++n) {
+  // One 64-key tile: block 0 (scores in sa) while block 1's scores go to sb,
+  // then block 1 while block 0 of the next tile goes to sa.  Only a slot's
+  // last tile is ragged and gets the tail mask.
+  auto tile = [&](int n) __attribute__((always_inline)) {
     const char* st = lds + (n % NS) * C::STAGE;
     const int valid = cur.valid();
-    // Block 0 of tile n (scores in sa) -> scores of block 1 into sb.
     {
       bf16x8 pop[QB][2];
       qk_block<HD, QB>(st, 1, qop, sb, lane);
@@ -385,7 +418,6 @@ void wave_attn_kernel(AttnArgs a) {
       if (valid < 64) mask_block<QB>(sb, valid - 32, lane);
       check(sb);
     }
-    // Block 1 of tile n (scores in sb) -> scores of block 0 of tile n+1 into sa.
     {
       bf16x8 pop[QB][2];
       const bool has_next = n + 1 < total_tiles;
@@ -403,7 +435,9 @@ void wave_attn_kernel(AttnArgs a) {
         check(sa);
       }
     }
-  }
+  };
+
+  for (int n = 0; n < total_tiles; ++n) tile(n);
 
   // Epilogue: O = O^T / l, LSE = ln2 * (mref + log2 l).
   __bf16* out = static_cast<__bf16*>(a.o);
