@@ -31,6 +31,8 @@
 // with two waves per SIMD the hardware interleaves them as well.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace wave {
@@ -173,8 +175,12 @@ __device__ __forceinline__ void qk_block(const char* ks, int kb, const bf16x8 (&
 }
 
 // Keys at or beyond `valid` (counted from the block's first key) get -inf.
+// Called under a wave-uniform branch that is true for one block in ~70; the
+// empty volatile asm keeps the compiler from if-converting the branch into
+// per-element selects executed for every block.
 template <int QB>
 __device__ __forceinline__ void mask_block(f32x16 (&s)[QB], int valid, int lane) {
+  asm volatile("");
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -407,8 +413,12 @@ void wave_attn_kernel(AttnArgs a) {
   // One 64-key tile: block 0 (scores in sa) while block 1's scores go to sb,
   // then block 1 while block 0 of the next tile goes to sa.  Only a slot's
   // last tile is ragged and gets the tail mask.
-  auto tile = [&](int n) __attribute__((always_inline)) {
-    const char* st = lds + (n % NS) * C::STAGE;
+  // The ring stage of tile n is n % NS; the loop below is unrolled NS times
+  // so that it is a compile-time constant and every LDS operand address is a
+  // per-lane base plus an immediate offset.
+  auto tile = [&](int n, auto stage_tag) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage_tag)::value;
+    const char* st = lds + ST * C::STAGE;
     const int valid = cur.valid();
     {
       bf16x8 pop[QB][2];
@@ -424,8 +434,8 @@ void wave_attn_kernel(AttnArgs a) {
       if (has_next) {
         wait_tiles(min(total_tiles - 2 - n, NS - 3));
         barrier();
-        if (n + NS - 1 < total_tiles) issue((n + NS - 1) % NS);
-        qk_block<HD, QB>(lds + ((n + 1) % NS) * C::STAGE, 0, qop, sa, lane);
+        if (n + NS - 1 < total_tiles) issue((ST + NS - 1) % NS);
+        qk_block<HD, QB>(lds + ((ST + 1) % NS) * C::STAGE, 0, qop, sa, lane);
       }
       softmax_block<QB>(sb, c2, mref, pop, l);
       pv_block<HD, QB>(st + C::KBYTES, 1, pop, o, lane);
@@ -437,7 +447,13 @@ void wave_attn_kernel(AttnArgs a) {
     }
   };
 
-  for (int n = 0; n < total_tiles; ++n) tile(n);
+  static_assert(NS == 4, "the tile loop below is unrolled for a 4-stage ring");
+  for (int n = 0; n < total_tiles; n += NS) {
+    tile(n, std::integral_constant<int, 0>{});
+    if (n + 1 < total_tiles) tile(n + 1, std::integral_constant<int, 1>{});
+    if (n + 2 < total_tiles) tile(n + 2, std::integral_constant<int, 2>{});
+    if (n + 3 < total_tiles) tile(n + 3, std::integral_constant<int, 3>{});
+  }
 
   // Epilogue: O = O^T / l, LSE = ln2 * (mref + log2 l).
   __bf16* out = static_cast<__bf16*>(a.o);
