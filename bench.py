@@ -11,7 +11,8 @@ tokens per 3-latent-frame chunk, 7 chunks), K=4 levels, progressive history,
 pipelined round 6: R(2), U(3,1), U(4,2), U(5,3), U(6,4) over 32,760 keys.
 
 Prints ONE JSON line on stdout.  Extra flags:
-  --workload {2,4,5}     2 (default), 4 = long video steady round, 5 = Wan-Streamer round
+  --workload {2,4,5,6}   2 (default), 4 = long video steady round, 5 = Wan-Streamer round,
+                         6 = Wan-Streamer audio decode (64 query rows per chunk, split-KV)
   --no-cpu-baseline      skip the CPU oracle timing
   --copy-calibration     also run one 1 GiB device copy (HBM counter calibration)
 """
@@ -56,7 +57,7 @@ def kv_write_bytes(plan, t, heads, head_dim, lpad, src_bytes=2):
 
 
 HBM_PROFILES = {2: "wave_attn_wan13b_round6_hbm.md", 4: "wave_attn_longvideo_round16_hbm.md",
-                5: "wave_attn_streamer_round7_hbm.md"}
+                5: "wave_attn_streamer_round7_hbm.md", 6: "wave_attn_streamer_audio_decode_hbm.md"}
 
 
 def traffic_from_profile(workload):
@@ -84,6 +85,19 @@ def traffic_from_profile(workload):
         return None
 
 
+def attention_bytes(plan, t, heads, head_dim):
+    """Compulsory HBM bytes of one round's attention: Q and O (bf16), the LSE,
+    and each distinct cache slot the round's gather lists read (K and V)."""
+    slots = {}
+    rows = 0
+    for n in plan.round_nodes(t):
+        rows += int(n[5])
+        for c in plan.node_ctx(n):
+            slots[(int(c[0]), int(c[1]))] = int(c[3])
+    kv = sum(slots.values()) * heads * head_dim * 2 * 2
+    return kv + rows * heads * head_dim * 2 * 2 + rows * heads * 4
+
+
 def sample_rows(L, n, seed=1234):
     rng = np.random.default_rng(seed)
     must = set(range(min(8, L))) | set(range(max(0, L - 8), L))
@@ -96,9 +110,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, choices=(2, 4, 5))
+    ap.add_argument("--workload", type=int, default=2, choices=(2, 4, 5, 6))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=128, help="query rows per node for the CPU oracle")
+    ap.add_argument("--cpu-rows", type=int, default=768,
+                    help="query rows per node for the CPU oracle (bounded sample, ~10-30 s of CPU work)")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -119,7 +134,8 @@ def main():
 
     t0 = time.perf_counter()
     plan = wv.wave_plan(B=w.B, K=w.K, policy=policy, sched=wv.WAVE, chunk_len=w.chunk_len,
-                        cond_len=w.cond_len, history_cap=w.history_cap)
+                        cond_len=w.cond_len, history_cap=w.history_cap, query_len=w.query_len)
+    decode = w.query_len > 0
     plan_ms = (time.perf_counter() - t0) * 1e3
     desc = plan.upload(device)
     lpad = plan.lpad()
@@ -137,7 +153,9 @@ def main():
         wv.kv_write(plan, desc, t, cache, k_src, v_src)
     k_src, v_src = fresh(t_meas)
     nodes = plan.round_nodes(t_meas).tolist()
-    q = torch.cat([wi.device_tensor(w, layer, n[0], n[1], "q", device, policy) for n in nodes])
+    qlen = w.query_len or w.chunk_len
+    # decode-shaped: the last query_len tokens of each chunk (its audio latents)
+    q = torch.cat([wi.device_tensor(w, layer, n[0], n[1], "q", device, policy)[-qlen:] for n in nodes])
     rows = int(plan.round_q_rows[t_meas])
     o = torch.empty((rows, w.heads, w.head_dim), dtype=torch.bfloat16, device=device)
     lse = torch.empty((w.heads, rows), dtype=torch.float32, device=device)
@@ -145,12 +163,24 @@ def main():
 
     flops = algorithmic_flops(plan, t_meas, w.heads, w.head_dim)
     kvw_bytes = kv_write_bytes(plan, t_meas, w.heads, w.head_dim, lpad)
+    attn_bytes = attention_bytes(plan, t_meas, w.heads, w.head_dim)
+    workspace = None
+    splits = 1
+    if decode:
+        nbytes, splits = wv.splitkv_workspace_bytes(plan, t_meas, w.heads, w.head_dim, 0)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+    def attn(stream):
+        if decode:
+            return wv.wave_attn_splitkv(plan, desc, t_meas, cache, q, w.scale, num_splits=splits,
+                                        workspace=workspace, o=o, lse=lse, stream=stream)
+        return wv.wave_attn(plan, desc, t_meas, cache, q, w.scale, o=o, lse=lse, stream=stream)
 
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
             wv.kv_write(plan, desc, t_meas, cache, k_src, v_src, stream=stream)
-            wv.wave_attn(plan, desc, t_meas, cache, q, w.scale, o=o, lse=lse, stream=stream)
+            attn(stream)
         torch.cuda.synchronize()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
                 torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -160,7 +190,7 @@ def main():
             e0.record(stream)
             wv.kv_write(plan, desc, t_meas, cache, k_src, v_src, stream=stream)
             e1.record(stream)
-            wv.wave_attn(plan, desc, t_meas, cache, q, w.scale, o=o, lse=lse, stream=stream)
+            attn(stream)
             e2.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -174,11 +204,14 @@ def main():
     attn_avg = float(attn_ms.mean())
     achieved = flops / (attn_avg * 1e-3) / 1e12
     value = flops / (ms_per_step * 1e-3) / 1e12
+    attn_gbps = attn_bytes / (attn_avg * 1e-3) / 1e9
     eprint(f"[bench] {w.name}: round {t_meas}, {len(nodes)} nodes, {rows} query rows, "
            f"{flops / 1e12:.3f} TFLOP")
     eprint(f"[bench] wave_attn {attn_avg:.3f} ms (p10 {np.percentile(attn_ms, 10):.3f}, "
            f"p90 {np.percentile(attn_ms, 90):.3f}) = {achieved:.1f} TFLOP/s = "
            f"{100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak")
+    eprint(f"[bench] wave_attn moves {attn_bytes / 1e6:.1f} MB compulsory = {attn_gbps:.0f} GB/s"
+           + (f" (split-KV, {splits} splits)" if decode else ""))
     eprint(f"[bench] kv_write {kvw_ms.mean() * 1e3:.1f} us = {kvw_bytes / (kvw_ms.mean() * 1e-3) / 1e9:.0f} GB/s; "
            f"step {ms_per_step:.3f} ms wall")
 
@@ -220,7 +253,8 @@ def main():
             "policy": wi.POLICY_NAMES[policy],
             "chunks": w.B, "levels": w.K, "chunk_tokens": w.chunk_len, "cond_tokens": w.cond_len,
             "heads": w.heads, "head_dim": w.head_dim, "history_cap": w.history_cap,
-            "nodes_in_round": len(nodes), "query_rows": rows,
+            "nodes_in_round": len(nodes), "query_rows": rows, "query_rows_per_node": qlen,
+            "splitkv_splits": splits if decode else None,
             "algorithmic_tflop": round(flops / 1e12, 4),
         },
         "attn_ms": round(attn_avg, 4),
@@ -229,14 +263,23 @@ def main():
         "pct_bf16_peak": round(100 * achieved / PEAK_BF16_TFLOPS, 2),
         "kv_write_gbps": round(kvw_bytes / (kvw_ms.mean() * 1e-3) / 1e9, 1),
         "plan_ms": round(plan_ms, 3),
-        "roofline": {
+        "roofline": ({
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic_from_profile(args.workload),
-        },
+        } if not decode else {
+            "bound": "hbm",
+            "achieved": round(attn_gbps, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(attn_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": traffic_from_profile(args.workload),
+        }),
+        "attn_compulsory_mb": round(attn_bytes / 1e6, 2),
+        "attn_gbps": round(attn_gbps, 1),
         "cpu_baseline": cpu,
     }
     if copy_ms is not None:
@@ -257,10 +300,11 @@ def cpu_baseline(w, plan, t_meas, nodes, policy, layer, device, rows_per_node):
     except Exception:
         threads = len(os.sched_getaffinity(0))
 
-    p = op.Params(w.B, w.K, policy, op.SERIAL, w.history_cap, w.chunk_len, w.cond_len)
+    qlen = w.query_len or w.chunk_len
+    p = op.Params(w.B, w.K, policy, op.SERIAL, w.history_cap, w.chunk_len, w.cond_len, w.query_len)
     oplan = op.oracle_plan(p)
     want = {(n[0], n[1]) for n in nodes}
-    rows = sample_rows(w.chunk_len, rows_per_node)
+    rows = sample_rows(qlen, rows_per_node)
     # Every slot the serial rollout writes until it reaches the wanted nodes:
     # fetched from the seeded generator before the clock starts.
     need = set()
@@ -278,8 +322,8 @@ def cpu_baseline(w, plan, t_meas, nodes, policy, layer, device, rows_per_node):
         k = wi.device_tensor(w, layer, c, lv, "k", device, policy).float().cpu().numpy().astype(np.float64)
         v = wi.device_tensor(w, layer, c, lv, "v", device, policy).float().cpu().numpy().astype(np.float64)
         kv[(c, lv)] = (k, v)
-    qs = {(c, lv): wi.device_tensor(w, layer, c, lv, "q", device, policy).float().cpu().numpy().astype(np.float64)
-          for (c, lv) in want}
+    qs = {(c, lv): wi.device_tensor(w, layer, c, lv, "q", device, policy)[-qlen:].float().cpu().numpy()
+          .astype(np.float64) for (c, lv) in want}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     out = rollout(p, oplan, lambda c, lv: qs[(c, lv)], lambda c, lv: kv[(c, lv)], w.scale,
@@ -296,7 +340,7 @@ def cpu_baseline(w, plan, t_meas, nodes, policy, layer, device, rows_per_node):
         "kind": "oracle",
         "sample": f"{len(rows)} query rows of each of the {len(nodes)} nodes of round {t_meas}, "
                   f"all {w.heads} heads, fp64 dense-mask attention over every live slot; "
-                  f"{secs:.1f} s wall; full-round estimate {secs * w.chunk_len / len(rows):.0f} s",
+                  f"{secs:.1f} s wall; full-round estimate {secs * qlen / len(rows):.0f} s",
     }
 
 

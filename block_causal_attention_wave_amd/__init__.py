@@ -27,7 +27,8 @@ from ._lib import (WAVE_CLEAN, WAVE_DTYPE_BF16, WAVE_DTYPE_FP32, WAVE_KEY_TILE, 
 CLEAN, SAME_LEVEL, PROGRESSIVE = WAVE_CLEAN, WAVE_SAME_LEVEL, WAVE_PROGRESSIVE
 SERIAL, WAVE = WAVE_SCHED_SERIAL, WAVE_SCHED_WAVE
 
-__all__ = ["Plan", "KVCache", "wave_plan", "kv_write", "wave_attn", "WaveError",
+__all__ = ["Plan", "KVCache", "wave_plan", "kv_write", "wave_attn", "wave_attn_splitkv",
+           "splitkv_workspace_bytes", "WaveError",
            "CLEAN", "SAME_LEVEL", "PROGRESSIVE", "SERIAL", "WAVE", "WAVE_LEVEL_COND",
            "WAVE_Q_TILE", "WAVE_KEY_TILE", "WAVE_NODE_UPDATE", "WAVE_NODE_REFRESH"]
 
@@ -49,11 +50,12 @@ class Plan:
     work : [*, 4] node, q_start, q_rows, keys
     """
 
-    def __init__(self, B, K, policy, sched, chunk_len, history_cap=-1, cond_len=0, q_tile=0):
+    def __init__(self, B, K, policy, sched, chunk_len, history_cap=-1, cond_len=0, q_tile=0,
+                 query_len=0):
         lib = _lib.load()
         self.params = dict(B=B, K=K, policy=policy, sched=sched, history_cap=history_cap,
-                           chunk_len=chunk_len, cond_len=cond_len, q_tile=q_tile)
-        p = _lib.PlanParams(B, K, policy, sched, history_cap, chunk_len, cond_len, q_tile)
+                           chunk_len=chunk_len, cond_len=cond_len, q_tile=q_tile, query_len=query_len)
+        p = _lib.PlanParams(B, K, policy, sched, history_cap, chunk_len, cond_len, q_tile, query_len)
         h = C.c_void_p()
         _lib.check(lib.wave_plan(C.byref(p), C.byref(h)))
         self._h = h
@@ -166,9 +168,7 @@ def kv_write(plan: Plan, d_desc, round: int, cache: KVCache, k_src, v_src, strea
                                     _dtype_code(k_src), k_src.stride(0), _stream_ptr(stream)))
 
 
-def wave_attn(plan: Plan, d_desc, round: int, cache: KVCache, q, scale: float, o=None, lse=None,
-              want_lse=True, stream=None):
-    """Attention of round `round`: q [rows, heads, d] (bf16 or fp32) -> (o bf16, lse fp32 [heads, rows])."""
+def _attn_outputs(plan, round, cache, q, o, lse, want_lse):
     import torch
     rows = int(plan.round_q_rows[round]) if 0 <= round < plan.num_rounds else 0
     _check_rows(q, rows, cache.heads, cache.head_dim, "q")
@@ -181,9 +181,42 @@ def wave_attn(plan: Plan, d_desc, round: int, cache: KVCache, q, scale: float, o
     elif lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
                               or tuple(lse.shape) != (cache.heads, rows)):
         raise ValueError("lse must be a contiguous fp32 [heads, rows] tensor")
+    return o, lse
+
+
+def wave_attn(plan: Plan, d_desc, round: int, cache: KVCache, q, scale: float, o=None, lse=None,
+              want_lse=True, stream=None):
+    """Attention of round `round`: q [rows, heads, d] (bf16 or fp32) -> (o bf16, lse fp32 [heads, rows])."""
+    o, lse = _attn_outputs(plan, round, cache, q, o, lse, want_lse)
     _lib.check(_lib.load().wave_attn(plan.handle, C.c_void_p(d_desc.data_ptr()), round, C.byref(cache.c),
                                      C.c_void_p(q.data_ptr()), _dtype_code(q), q.stride(0),
                                      C.c_void_p(o.data_ptr()),
                                      C.c_void_p(lse.data_ptr() if lse is not None else 0),
                                      float(scale), _stream_ptr(stream)))
+    return o, lse
+
+
+def splitkv_workspace_bytes(plan: Plan, round: int, heads: int, head_dim: int, num_splits: int = 0):
+    """(bytes, splits) of the split-KV workspace for this round (num_splits 0 = library's choice)."""
+    b = C.c_size_t()
+    s = C.c_int32()
+    _lib.check(_lib.load().wave_attn_splitkv_workspace(plan.handle, round, heads, head_dim, num_splits,
+                                                       C.byref(b), C.byref(s)))
+    return b.value, s.value
+
+
+def wave_attn_splitkv(plan: Plan, d_desc, round: int, cache: KVCache, q, scale: float, num_splits: int = 0,
+                      workspace=None, o=None, lse=None, want_lse=True, stream=None):
+    """Split-KV attention of round `round` (short queries, long contexts); same results as wave_attn."""
+    import torch
+    o, lse = _attn_outputs(plan, round, cache, q, o, lse, want_lse)
+    nbytes, splits = splitkv_workspace_bytes(plan, round, cache.heads, cache.head_dim, num_splits)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _lib.check(_lib.load().wave_attn_splitkv(plan.handle, C.c_void_p(d_desc.data_ptr()), round,
+                                             C.byref(cache.c), C.c_void_p(q.data_ptr()), _dtype_code(q),
+                                             q.stride(0), C.c_void_p(o.data_ptr()),
+                                             C.c_void_p(lse.data_ptr() if lse is not None else 0),
+                                             float(scale), splits, C.c_void_p(workspace.data_ptr()),
+                                             workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
     return o, lse

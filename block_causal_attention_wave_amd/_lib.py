@@ -23,12 +23,14 @@ WAVE_Q_TILE = 256
 WAVE_KEY_TILE = 64
 
 EXPORTS = ("wave_plan", "wave_plan_view_get", "wave_plan_desc_size", "wave_plan_desc_pack",
-           "wave_plan_destroy", "kv_write", "wave_attn", "wave_last_error")
+           "wave_plan_destroy", "kv_write", "wave_attn", "wave_attn_splitkv_workspace",
+           "wave_attn_splitkv", "wave_last_error")
 
 
 class PlanParams(C.Structure):
     _fields_ = [(n, C.c_int32) for n in
-                ("B", "K", "policy", "sched", "history_cap", "chunk_len", "cond_len", "q_tile")]
+                ("B", "K", "policy", "sched", "history_cap", "chunk_len", "cond_len", "q_tile",
+                 "query_len")]
 
 
 class SlotRef(C.Structure):
@@ -96,6 +98,13 @@ def load() -> C.CDLL:
                               C.c_void_p, C.c_int32, C.c_int64, C.c_void_p, C.c_void_p,
                               C.c_float, C.c_void_p]
     lib.wave_attn.restype = C.c_int32
+    lib.wave_attn_splitkv_workspace.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                                C.POINTER(C.c_size_t), C.POINTER(C.c_int32)]
+    lib.wave_attn_splitkv_workspace.restype = C.c_int32
+    lib.wave_attn_splitkv.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.POINTER(KvCache),
+                                      C.c_void_p, C.c_int32, C.c_int64, C.c_void_p, C.c_void_p,
+                                      C.c_float, C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p]
+    lib.wave_attn_splitkv.restype = C.c_int32
     lib.wave_last_error.argtypes = []
     lib.wave_last_error.restype = C.c_char_p
     _lib = lib

@@ -2,6 +2,7 @@
 // No C++ exception crosses this boundary; every entry point returns a status.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -151,30 +152,61 @@ int32_t kv_write(const wave_plan_t* plan, const void* d_desc, int32_t round, con
   return ok();
 }
 
-int32_t wave_attn(const wave_plan_t* plan, const void* d_desc, int32_t round, const wave_kv_cache* cache,
-                  const void* q, int32_t q_dtype, int64_t q_row_stride, void* o, float* lse, float scale,
-                  void* stream) {
-  int32_t rc = check_common(plan, d_desc, round, cache, "wave_attn");
+}  // extern "C"
+
+namespace {
+
+// Splits for split-KV attention: enough workgroups for about two per compute
+// unit, at most 64 splits.
+int32_t auto_splits(const wave::Plan& p, int32_t round, int32_t heads) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  const int64_t items = static_cast<int64_t>(p.round_work_begin[round + 1] - p.round_work_begin[round]) * heads;
+  if (items <= 0) return 1;
+  int64_t s = (2 * static_cast<int64_t>(cus) + items - 1) / items;
+  return static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(s, 64)));
+}
+
+constexpr size_t kAlign = 256;
+
+size_t splitkv_bytes(const wave::Plan& p, int32_t round, int32_t heads, int32_t head_dim, int32_t splits,
+                     size_t* lse_offset) {
+  const size_t rows = static_cast<size_t>(p.round_q_rows[round]);
+  const size_t o_bytes = static_cast<size_t>(splits) * rows * heads * head_dim * sizeof(float);
+  const size_t off = (o_bytes + kAlign - 1) / kAlign * kAlign;
+  if (lse_offset) *lse_offset = off;
+  return off + static_cast<size_t>(splits) * heads * rows * sizeof(float);
+}
+
+int32_t attn_common(const wave_plan_t* plan, const void* d_desc, int32_t round, const wave_kv_cache* cache,
+                    const void* q, int32_t q_dtype, int64_t q_row_stride, void* o, float* lse, float scale,
+                    const char* fn, wave::AttnArgs& a) {
+  int32_t rc = check_common(plan, d_desc, round, cache, fn);
   if (rc != WAVE_OK) return rc;
+  const std::string f(fn);
   const wave::Plan& p = plan->p;
-  if (!q || !o) return set_error(WAVE_ERR_INVALID_ARG, "wave_attn: null q or o");
+  if (!q || !o) return set_error(WAVE_ERR_INVALID_ARG, f + ": null q or o");
   if (p.params.q_tile != WAVE_Q_TILE)
-    return set_error(WAVE_ERR_UNSUPPORTED, "wave_attn: plan q_tile must be WAVE_Q_TILE");
-  if (p.max_ctx > 512) return set_error(WAVE_ERR_UNSUPPORTED, "wave_attn: gather lists longer than 512 slots");
+    return set_error(WAVE_ERR_UNSUPPORTED, f + ": plan q_tile must be WAVE_Q_TILE");
+  if (p.max_ctx > 512) return set_error(WAVE_ERR_UNSUPPORTED, f + ": gather lists longer than 512 slots");
   if (q_dtype != WAVE_DTYPE_BF16 && q_dtype != WAVE_DTYPE_FP32)
-    return set_error(WAVE_ERR_UNSUPPORTED, "wave_attn: q_dtype must be WAVE_DTYPE_BF16 or WAVE_DTYPE_FP32");
+    return set_error(WAVE_ERR_UNSUPPORTED, f + ": q_dtype must be WAVE_DTYPE_BF16 or WAVE_DTYPE_FP32");
   const int64_t row = static_cast<int64_t>(cache->heads) * cache->head_dim;
-  if (q_row_stride < row) return set_error(WAVE_ERR_INVALID_ARG, "wave_attn: q_row_stride < heads*head_dim");
+  if (q_row_stride < row) return set_error(WAVE_ERR_INVALID_ARG, f + ": q_row_stride < heads*head_dim");
   const int64_t esz = q_dtype == WAVE_DTYPE_FP32 ? 4 : 2;
-  if (!aligned16(q) || (q_row_stride * esz) % 16 != 0 || (reinterpret_cast<uintptr_t>(o) & 7u) != 0 ||
+  if (!aligned16(q) || (q_row_stride * esz) % 16 != 0 || !aligned16(o) ||
       (lse && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0))
-    return set_error(WAVE_ERR_UNSUPPORTED, "wave_attn: q must be 16-byte aligned (rows too), o 8-byte, lse 4-byte");
-  if (!std::isfinite(scale)) return set_error(WAVE_ERR_INVALID_ARG, "wave_attn: scale must be finite");
+    return set_error(WAVE_ERR_UNSUPPORTED, f + ": q, o and q's rows must be 16-byte aligned, lse 4-byte");
+  if (!std::isfinite(scale)) return set_error(WAVE_ERR_INVALID_ARG, f + ": scale must be finite");
   const int32_t k0 = p.round_work_begin[round], k1 = p.round_work_begin[round + 1];
-  if (static_cast<int64_t>(k1 - k0) * cache->heads > INT32_MAX)
-    return set_error(WAVE_ERR_UNSUPPORTED, "wave_attn: too many work items");
+  if (static_cast<int64_t>(k1 - k0) * cache->heads * 64 > INT32_MAX)
+    return set_error(WAVE_ERR_UNSUPPORTED, f + ": too many work items");
   const int32_t* desc = static_cast<const int32_t*>(d_desc);
-  wave::AttnArgs a{};
+  a = wave::AttnArgs{};
   a.nodes = desc + p.desc[8];
   a.ctx = desc + p.desc[9];
   a.work = desc + p.desc[11];
@@ -192,8 +224,69 @@ int32_t wave_attn(const wave_plan_t* plan, const void* d_desc, int32_t round, co
   a.lse = lse;
   a.lse_stride = p.round_q_rows[round];
   a.scale_log2e = scale * 1.4426950408889634f;
+  a.num_splits = 1;
+  return WAVE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t wave_attn(const wave_plan_t* plan, const void* d_desc, int32_t round, const wave_kv_cache* cache,
+                  const void* q, int32_t q_dtype, int64_t q_row_stride, void* o, float* lse, float scale,
+                  void* stream) {
+  wave::AttnArgs a;
+  const int32_t rc = attn_common(plan, d_desc, round, cache, q, q_dtype, q_row_stride, o, lse, scale,
+                                 "wave_attn", a);
+  if (rc != WAVE_OK) return rc;
   const hipError_t e = wave::launch_wave_attn(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return set_error(WAVE_ERR_HIP, std::string("wave_attn: ") + hipGetErrorString(e));
+  return ok();
+}
+
+int32_t wave_attn_splitkv_workspace(const wave_plan_t* plan, int32_t round, int32_t heads, int32_t head_dim,
+                                    int32_t num_splits, size_t* bytes, int32_t* splits_used) {
+  if (!plan || !bytes) return set_error(WAVE_ERR_INVALID_ARG, "wave_attn_splitkv_workspace: null argument");
+  const wave::Plan& p = plan->p;
+  if (round < 0 || round >= p.num_rounds())
+    return set_error(WAVE_ERR_INVALID_ARG, "wave_attn_splitkv_workspace: round out of range");
+  if (heads < 1 || head_dim < 1 || num_splits < 0 || num_splits > 4096)
+    return set_error(WAVE_ERR_INVALID_ARG, "wave_attn_splitkv_workspace: bad heads, head_dim or num_splits");
+  const int32_t s = num_splits == 0 ? auto_splits(p, round, heads) : num_splits;
+  *bytes = splitkv_bytes(p, round, heads, head_dim, s, nullptr);
+  if (splits_used) *splits_used = s;
+  return ok();
+}
+
+int32_t wave_attn_splitkv(const wave_plan_t* plan, const void* d_desc, int32_t round, const wave_kv_cache* cache,
+                          const void* q, int32_t q_dtype, int64_t q_row_stride, void* o, float* lse, float scale,
+                          int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  wave::AttnArgs a;
+  const int32_t rc = attn_common(plan, d_desc, round, cache, q, q_dtype, q_row_stride, o, lse, scale,
+                                 "wave_attn_splitkv", a);
+  if (rc != WAVE_OK) return rc;
+  if (num_splits < 0 || num_splits > 4096)
+    return set_error(WAVE_ERR_INVALID_ARG, "wave_attn_splitkv: num_splits must be in [0, 4096]");
+  const wave::Plan& p = plan->p;
+  const int32_t s = num_splits == 0 ? auto_splits(p, round, cache->heads) : num_splits;
+  size_t lse_off = 0;
+  const size_t need = splitkv_bytes(p, round, cache->heads, cache->head_dim, s, &lse_off);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+    return set_error(WAVE_ERR_INVALID_ARG, "wave_attn_splitkv: workspace must be non-null and 256-byte aligned");
+  if (workspace_bytes < need)
+    return set_error(WAVE_ERR_CAPACITY, "wave_attn_splitkv: workspace smaller than wave_attn_splitkv_workspace()");
+  if (static_cast<int64_t>(a.num_work) * cache->heads * s > INT32_MAX)
+    return set_error(WAVE_ERR_UNSUPPORTED, "wave_attn_splitkv: too many workgroups");
+  a.num_splits = s;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + lse_off);
+  if (s == 1) {
+    // one split: the plain kernel writes o and lse directly
+    a.part_o = nullptr;
+    a.part_lse = nullptr;
+  }
+  const hipError_t e = wave::launch_wave_attn(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return set_error(WAVE_ERR_HIP, std::string("wave_attn_splitkv: ") + hipGetErrorString(e));
   return ok();
 }
 

@@ -38,6 +38,12 @@ struct AttnArgs {
   float* lse;
   int32_t lse_stride;  // rows of the round (LSE is [heads][rows])
   float scale_log2e;   // scale * log2(e)
+  // split-KV: > 1 splits each node's key tiles into that many contiguous
+  // ranges; partial results go to part_o (fp32 [splits][rows][heads][d]) and
+  // part_lse (fp32 [splits][heads][rows]) and are merged into o / lse.
+  int32_t num_splits;
+  float* part_o;
+  float* part_lse;
 };
 
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);

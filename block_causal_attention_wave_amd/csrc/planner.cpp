@@ -56,6 +56,7 @@ bool fail(std::string* err, const char* msg) {
 int32_t build_plan(const wave_plan_params& pin, Plan& out, std::string* err) {
   wave_plan_params p = pin;
   if (p.q_tile == 0) p.q_tile = WAVE_Q_TILE;
+  if (p.query_len == 0) p.query_len = p.chunk_len;
   if (p.B < 1 || p.K < 1 || p.B > (1 << 16) || p.K > (1 << 12)) {
     fail(err, "wave_plan: need 1 <= B <= 65536 and 1 <= K <= 4096");
     return WAVE_ERR_INVALID_ARG;
@@ -68,8 +69,8 @@ int32_t build_plan(const wave_plan_params& pin, Plan& out, std::string* err) {
     fail(err, "wave_plan: unknown schedule");
     return WAVE_ERR_INVALID_ARG;
   }
-  if (p.history_cap < -1 || p.chunk_len < 1 || p.cond_len < 0 || p.q_tile < 1) {
-    fail(err, "wave_plan: need history_cap >= -1, chunk_len >= 1, cond_len >= 0, q_tile >= 0");
+  if (p.history_cap < -1 || p.chunk_len < 1 || p.cond_len < 0 || p.q_tile < 1 || p.query_len < 1) {
+    fail(err, "wave_plan: need history_cap >= -1, chunk_len >= 1, cond_len >= 0, q_tile >= 0, query_len >= 0");
     return WAVE_ERR_INVALID_ARG;
   }
   if (static_cast<int64_t>(p.B) * (p.K + 1) > (1 << 24)) {
@@ -224,7 +225,7 @@ int32_t build_plan(const wave_plan_params& pin, Plan& out, std::string* err) {
       v.kind = n.kind;
       v.round = t;
       v.q_offset = static_cast<int32_t>(q_off);
-      v.q_len = p.chunk_len;
+      v.q_len = p.query_len;
       v.ctx_begin = static_cast<int32_t>(pl.ctx.size());
       v.ctx_count = static_cast<int32_t>(n.reads.size());
       v.write_begin = static_cast<int32_t>(pl.writes.size());
@@ -234,7 +235,7 @@ int32_t build_plan(const wave_plan_params& pin, Plan& out, std::string* err) {
         pl.writes.push_back({s.chunk, s.level, phys[slot_index(s)], len_of(s)});
         src_off += len_of(s);
       }
-      q_off += p.chunk_len;
+      q_off += p.query_len;
       pl.max_ctx = std::max(pl.max_ctx, v.ctx_count);
       pl.nodes.push_back(v);
     }

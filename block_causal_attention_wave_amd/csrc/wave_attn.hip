@@ -278,9 +278,31 @@ struct Walker {
       ++t;
     }
   }
+  // Advance k tiles, whole slots at a time.
+  __device__ __forceinline__ void skip(int k) {
+    while (k > 0 && e < count) {
+      const int left = (len_ + kKT - 1) / kKT - t;
+      if (k >= left) {
+        k -= left;
+        ++e;
+        t = 0;
+        load();
+      } else {
+        t += k;
+        k = 0;
+      }
+    }
+  }
 };
 
-template <int HD, int W, int QB>
+// SPLIT = false: one workgroup per (work item, head) over the node's whole
+// gather list; writes bf16 O and the LSE.
+// SPLIT = true (split-KV, for short query chunks against long contexts):
+// one workgroup per (work item, head, key split) over a contiguous range of
+// the node's key tiles; writes fp32 O normalised over that range and its LSE,
+// merged afterwards by wave_attn_combine_kernel.  Waves whose 32-row blocks
+// hold no query row skip the arithmetic but keep loading tiles.
+template <int HD, int W, int QB, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * W, 64 * W), amdgpu_waves_per_eu(W / 4, W / 4)))
 void wave_attn_kernel(AttnArgs a) {
   using C = Cfg<HD, W, QB>;
@@ -290,7 +312,16 @@ void wave_attn_kernel(AttnArgs a) {
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int wv_u = __builtin_amdgcn_readfirstlane(wv);
-  const int item = blockIdx.x / a.heads, h = blockIdx.x % a.heads;
+  int item, h, split = 0;
+  if constexpr (SPLIT) {
+    const int hs = a.heads * a.num_splits;
+    item = blockIdx.x / hs;
+    h = (blockIdx.x % hs) / a.num_splits;
+    split = blockIdx.x % a.num_splits;
+  } else {
+    item = blockIdx.x / a.heads;
+    h = blockIdx.x % a.heads;
+  }
   const int32_t* wk = a.work + 4 * (a.work_begin + item);
   const int node = wk[0], q_start = wk[1], q_rows = wk[2];
   const int32_t* nd = a.nodes + 4 * node;
@@ -308,6 +339,19 @@ void wave_attn_kernel(AttnArgs a) {
   int total_tiles = 0;
   for (int e = 0; e < ctx_count; ++e) total_tiles += (ctx_lds[2 * e + 1] + kKT - 1) / kKT;
   total_tiles = __builtin_amdgcn_readfirstlane(total_tiles);
+  int first_tile = 0;
+  if constexpr (SPLIT) {
+    const int per = (total_tiles + a.num_splits - 1) / a.num_splits;
+    first_tile = min(total_tiles, split * per);
+    total_tiles = min(total_tiles, first_tile + per) - first_tile;
+    if (total_tiles <= 0) {  // empty range: weight zero in the merge
+      const int r = threadIdx.x;
+      if (r < q_rows)
+        a.part_lse[((int64_t)split * a.heads + h) * a.lse_stride + q_offset + q_start + r] = -INFINITY;
+      return;
+    }
+  }
+  const bool active = !SPLIT || wv * QB * 32 < q_rows;  // wave-uniform
 
   // Q fragments (B operand of S^T): lane holds query (lane & 31) of block qb,
   // dims 16c + 8*(lane>>5) .. +7.
@@ -351,6 +395,7 @@ void wave_attn_kernel(AttnArgs a) {
   for (int qb = 0; qb < QB; ++qb) l[qb] = 0.0f;
 
   Walker ld(ctx_lds, ctx_count);
+  ld.skip(first_tile);
   const TileOffsets<HD, W, QB> toff(lpad, wv, lane);
   auto issue = [&](int stage) {
     const int64_t slot = (int64_t)ld.phys() * slot_elems;
@@ -379,11 +424,14 @@ void wave_attn_kernel(AttnArgs a) {
   wait_tiles(min(total_tiles - 1, NS - 2));
   barrier();
   Walker cur(ctx_lds, ctx_count);
+  cur.skip(first_tile);
   f32x16 sa[QB], sb[QB];
-  qk_block<HD, QB>(lds, 0, qop, sa, lane);
-  if (cur.valid() < 32) mask_block<QB>(sa, cur.valid(), lane);
+  if (active) {
+    qk_block<HD, QB>(lds, 0, qop, sa, lane);
+    if (cur.valid() < 32) mask_block<QB>(sa, cur.valid(), lane);
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) mref[qb] = c2 * block_rowmax(sa[qb]);
+    for (int qb = 0; qb < QB; ++qb) mref[qb] = c2 * block_rowmax(sa[qb]);
+  }
 
   // Raise the reference if the freshly computed block exceeds it by more
   // than 2^kRescaleLog2 (wave-uniform branch; rare after the first blocks).
@@ -420,7 +468,7 @@ void wave_attn_kernel(AttnArgs a) {
     constexpr int ST = decltype(stage_tag)::value;
     const char* st = lds + ST * C::STAGE;
     const int valid = cur.valid();
-    {
+    if (active) {
       bf16x8 pop[QB][2];
       qk_block<HD, QB>(st, 1, qop, sb, lane);
       softmax_block<QB>(sa, c2, mref, pop, l);
@@ -435,12 +483,14 @@ void wave_attn_kernel(AttnArgs a) {
         wait_tiles(min(total_tiles - 2 - n, NS - 3));
         barrier();
         if (n + NS - 1 < total_tiles) issue((ST + NS - 1) % NS);
-        qk_block<HD, QB>(lds + ((ST + 1) % NS) * C::STAGE, 0, qop, sa, lane);
+        if (active) qk_block<HD, QB>(lds + ((ST + 1) % NS) * C::STAGE, 0, qop, sa, lane);
       }
-      softmax_block<QB>(sb, c2, mref, pop, l);
-      pv_block<HD, QB>(st + C::KBYTES, 1, pop, o, lane);
+      if (active) {
+        softmax_block<QB>(sb, c2, mref, pop, l);
+        pv_block<HD, QB>(st + C::KBYTES, 1, pop, o, lane);
+      }
       cur.next();
-      if (has_next) {
+      if (has_next && active) {
         if (cur.valid() < 32) mask_block<QB>(sa, cur.valid(), lane);
         check(sa);
       }
@@ -456,29 +506,82 @@ void wave_attn_kernel(AttnArgs a) {
   }
 
   // Epilogue: O = O^T / l, LSE = ln2 * (mref + log2 l).
-  __bf16* out = static_cast<__bf16*>(a.o);
+  if (!active) return;
   const int64_t orow_stride = (int64_t)a.heads * HD;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float ltot = halfwave_sum(l[qb]);
     const float inv = 1.0f / ltot;
+    const float lse = (mref[qb] + __log2f(ltot)) * 0.69314718055994531f;
     const int r = (wv * QB + qb) * 32 + (lane & 31);
     if (r < q_rows) {
       const int64_t grow = q_offset + q_start + r;
-      __bf16* orow = out + grow * orow_stride + (int64_t)h * HD;
+      if constexpr (SPLIT) {
+        float* orow = a.part_o + (((int64_t)split * a.lse_stride + grow) * a.heads + h) * HD;
 #pragma unroll
-      for (int db = 0; db < C::ND; ++db)
+        for (int db = 0; db < C::ND; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          bf16x4 v;
+          for (int g = 0; g < 4; ++g) {
+            f32x4 v;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = (__bf16)(o[db][qb][4 * g + i] * inv);
-          *reinterpret_cast<bf16x4*>(orow + db * 32 + g * 8 + (lane >> 5) * 4) = v;
-        }
-      if (a.lse != nullptr && lane < 32)
-        a.lse[(int64_t)h * a.lse_stride + grow] = (mref[qb] + __log2f(ltot)) * 0.69314718055994531f;
+            for (int i = 0; i < 4; ++i) v[i] = o[db][qb][4 * g + i] * inv;
+            *reinterpret_cast<f32x4*>(orow + db * 32 + g * 8 + (lane >> 5) * 4) = v;
+          }
+        if (lane < 32) a.part_lse[((int64_t)split * a.heads + h) * a.lse_stride + grow] = lse;
+      } else {
+        __bf16* orow = static_cast<__bf16*>(a.o) + grow * orow_stride + (int64_t)h * HD;
+#pragma unroll
+        for (int db = 0; db < C::ND; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            bf16x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = (__bf16)(o[db][qb][4 * g + i] * inv);
+            *reinterpret_cast<bf16x4*>(orow + db * 32 + g * 8 + (lane >> 5) * 4) = v;
+          }
+        if (a.lse != nullptr && lane < 32) a.lse[(int64_t)h * a.lse_stride + grow] = lse;
+      }
     }
   }
+}
+
+// Merge of split-KV partial results (one thread per row, head and 8 output
+// dims): with per-split LSE s_k and normalised partial outputs O_k,
+// LSE = log sum_k exp(s_k) and O = sum_k exp(s_k - LSE) O_k.  Splits with an
+// empty key range carry s_k = -inf and weigh nothing.
+template <int HD>
+__global__ __launch_bounds__(256) void wave_attn_combine_kernel(AttnArgs a) {
+  const int64_t rows = a.lse_stride;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int chunks = HD / 8;
+  if (t >= rows * a.heads * chunks) return;
+  const int ch = (int)(t % chunks);
+  const int64_t rh = t / chunks;
+  const int h = (int)(rh % a.heads);
+  const int64_t row = rh / a.heads;
+  const int S = a.num_splits;
+  float smax = -INFINITY;
+  for (int k = 0; k < S; ++k) smax = fmaxf(smax, a.part_lse[((int64_t)k * a.heads + h) * rows + row]);
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float wsum = 0.0f;
+  for (int k = 0; k < S; ++k) {
+    const float sk = a.part_lse[((int64_t)k * a.heads + h) * rows + row];
+    if (sk == -INFINITY) continue;
+    const float w = __expf(sk - smax);
+    wsum += w;
+    const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o + (((int64_t)k * rows + row) * a.heads + h) * HD + ch * 8);
+    const f32x4 x = src[0], y = src[1];
+    for (int i = 0; i < 4; ++i) {
+      acc[i] += w * x[i];
+      acc[4 + i] += w * y[i];
+    }
+  }
+  const float inv = 1.0f / wsum;
+  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+  bf16x8_t out;
+  for (int i = 0; i < 8; ++i) out[i] = (__bf16)(acc[i] * inv);
+  *reinterpret_cast<bf16x8_t*>(static_cast<__bf16*>(a.o) + (row * a.heads + h) * HD + ch * 8) = out;
+  if (ch == 0 && a.lse != nullptr) a.lse[(int64_t)h * rows + row] = smax + __logf(wsum);
 }
 
 #ifndef WAVE_ATTN_WAVES
@@ -491,10 +594,22 @@ constexpr int kQB = kQTile / (32 * kWaves);
 
 hipError_t launch_wave_attn(const AttnArgs& a, hipStream_t stream) {
   if (a.num_work == 0) return hipSuccess;
-  dim3 grid(a.num_work * a.heads);
   dim3 block(64 * kWaves);
-  if (a.head_dim == 128) hipLaunchKernelGGL((wave_attn_kernel<128, kWaves, kQB>), grid, block, 0, stream, a);
-  else hipLaunchKernelGGL((wave_attn_kernel<64, kWaves, kQB>), grid, block, 0, stream, a);
+  if (a.num_splits <= 1) {
+    dim3 grid(a.num_work * a.heads);
+    if (a.head_dim == 128) hipLaunchKernelGGL((wave_attn_kernel<128, kWaves, kQB, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((wave_attn_kernel<64, kWaves, kQB, false>), grid, block, 0, stream, a);
+    return hipGetLastError();
+  }
+  dim3 grid(a.num_work * a.heads * a.num_splits);
+  if (a.head_dim == 128) hipLaunchKernelGGL((wave_attn_kernel<128, kWaves, kQB, true>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((wave_attn_kernel<64, kWaves, kQB, true>), grid, block, 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t threads = (int64_t)a.lse_stride * a.heads * (a.head_dim / 8);
+  dim3 cgrid((unsigned)((threads + 255) / 256));
+  if (a.head_dim == 128) hipLaunchKernelGGL((wave_attn_combine_kernel<128>), cgrid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((wave_attn_combine_kernel<64>), cgrid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -81,6 +81,9 @@ typedef struct wave_plan_params {
   int32_t chunk_len;   /* tokens per chunk: query rows of a node, length of its slot, >= 1 */
   int32_t cond_len;    /* tokens of each conditioning slot C(i); 0 = no conditioning */
   int32_t q_tile;      /* query rows per work item; 0 = WAVE_Q_TILE */
+  int32_t query_len;   /* query rows of every node; 0 = chunk_len.  Fewer rows than the
+                          chunk's slot (e.g. only a chunk's audio tokens) give the
+                          decode-shaped case: short queries against long contexts. */
 } wave_plan_params;
 
 /* One logical cache slot as referenced by a node. */
@@ -94,7 +97,7 @@ typedef struct wave_slot_ref {
 typedef struct wave_node {
   int32_t chunk, level, kind, round;
   int32_t q_offset;    /* first row of this node in the round's packed Q / O */
-  int32_t q_len;       /* query rows (= chunk_len) */
+  int32_t q_len;       /* query rows (query_len, else chunk_len) */
   int32_t ctx_begin;   /* gather list: ctx[ctx_begin .. ctx_begin+ctx_count), timeline order, own slot last */
   int32_t ctx_count;
   int32_t write_begin; /* slots this node writes: writes[write_begin ..), conditioning first */
@@ -184,6 +187,30 @@ int32_t kv_write(const wave_plan_t* plan, const void* d_desc, int32_t round,
 int32_t wave_attn(const wave_plan_t* plan, const void* d_desc, int32_t round,
                   const wave_kv_cache* cache, const void* q, int32_t q_dtype,
                   int64_t q_row_stride, void* o, float* lse, float scale, void* stream);
+
+/* Split-KV attention for short query chunks against long contexts (the
+ * decode-shaped case: e.g. a chunk's 64 audio rows against tens of thousands
+ * of cached keys, Wan-Streamer v0.2 abstract and "Latency-Preserving
+ * Infrastructure": audio latents are short and handled unsharded).  Each
+ * node's key tiles (gather list order) are cut into num_splits contiguous
+ * ranges processed by separate workgroups; a second kernel merges them:
+ * LSE = log sum_k exp(LSE_k), O = sum_k exp(LSE_k - LSE) O_k.  Results equal
+ * wave_attn's up to rounding (the reduction order differs).
+ *   num_splits: >= 1, or 0 to let the library choose from the round's work
+ *               and the current device's compute-unit count.
+ *   workspace : device memory of at least wave_attn_splitkv_workspace()
+ *               bytes, 256-byte aligned, owned by the caller; its contents
+ *               need no initialisation and are scratch after the call.
+ * Other arguments as for wave_attn.  Asynchronous on `stream`; calls that
+ * share a workspace must be ordered on one stream. */
+int32_t wave_attn_splitkv_workspace(const wave_plan_t* plan, int32_t round, int32_t heads,
+                                    int32_t head_dim, int32_t num_splits, size_t* bytes,
+                                    int32_t* splits_used);
+int32_t wave_attn_splitkv(const wave_plan_t* plan, const void* d_desc, int32_t round,
+                          const wave_kv_cache* cache, const void* q, int32_t q_dtype,
+                          int64_t q_row_stride, void* o, float* lse, float scale,
+                          int32_t num_splits, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* Message of the last failed call on this thread ("" if none).  Valid until
  * the next call into this library from the same thread. */

@@ -58,6 +58,7 @@ class Params:
     history_cap: int = -1  # H: history window in chunks, -1 = unlimited
     chunk_len: int = 1     # tokens per chunk (query rows and latent slot length)
     cond_len: int = 0      # tokens of each chunk's conditioning slot, 0 = none
+    query_len: int = 0     # query rows per node, 0 = chunk_len (fewer: decode-shaped)
 
 
 def phi(policy: int, j: int, r: int) -> int:
@@ -240,14 +241,15 @@ def oracle_plan(p: Params) -> dict:
                 phys[s] = pid
                 capacity = max(capacity, pid + 1)
 
+    q_len = p.query_len if p.query_len > 0 else p.chunk_len
     round_node_begin = [0]
     nodes, ctx, writes = [], [], []
     for t, r in enumerate(rounds):
         q_off = 0
         for n in r:
-            nodes.append((n.chunk, n.level, n.kind, t, q_off, p.chunk_len,
+            nodes.append((n.chunk, n.level, n.kind, t, q_off, q_len,
                           len(ctx), len(n.ctx), len(writes), len(n.writes)))
-            q_off += p.chunk_len
+            q_off += q_len
             for s in n.ctx:
                 ctx.append((s[0], s[1], phys[s], slot_len(s)))
             for s in n.writes:

@@ -28,8 +28,9 @@ class HostInputs:
     """Seeded fp32 host tensors for small cases (Q/K/V ~ N(0, sigma^2))."""
 
     def __init__(self, key, heads, head_dim, chunk_len, cond_len, sigma=1.0, layer=0, policy=0,
-                 bf16=False):
+                 bf16=False, query_len=0):
         self.bf16 = bf16  # hand the kernels bf16-representable values
+        self.QL = query_len or chunk_len
         self.key, self.heads, self.hd = key, heads, head_dim
         self.L, self.C, self.sigma, self.layer, self.policy = chunk_len, cond_len, sigma, layer, policy
         self._cache = {}
@@ -37,7 +38,7 @@ class HostInputs:
     def _get(self, chunk, level, which):
         k = (chunk, level, which)
         if k not in self._cache:
-            n = self.L if which == "q" or level != wi.COND_LEVEL else self.C
+            n = self.QL if which == "q" else (self.C if level == wi.COND_LEVEL else self.L)
             seed = wi.tensor_seed(self.key, self.layer, chunk, level, which, self.policy)
             x = wi.host_normal(seed, (n, self.heads, self.hd), self.sigma)
             self._cache[k] = round_to_bf16(x) if self.bf16 else x
@@ -58,10 +59,11 @@ class HostInputs:
         return round_to_bf16(k).astype(np.float64), round_to_bf16(v).astype(np.float64)
 
 
-def gpu_rollout(plan, inputs, device, scale, src_dtype="fp32", poison=True, perturb=None):
+def gpu_rollout(plan, inputs, device, scale, src_dtype="fp32", poison=True, perturb=None, splits=None):
     """Run every round of `plan` on the GPU; return {(chunk, level): (O fp32 [L,h,d], LSE [h,L])}.
 
     perturb(chunk, level, k, v) -> (k, v) may alter the fresh K/V of a slot.
+    splits: None = wave_attn, else wave_attn_splitkv with that many splits (0 = auto).
     """
     import torch
     dt = torch.float32 if src_dtype == "fp32" else torch.bfloat16
@@ -82,7 +84,10 @@ def gpu_rollout(plan, inputs, device, scale, src_dtype="fp32", poison=True, pert
         wv.kv_write(plan, desc, t, cache, k_src, v_src)
         nodes = plan.round_nodes(t).tolist()
         q = torch.from_numpy(np.concatenate([inputs.q(n[0], n[1]) for n in nodes])).to(device=device, dtype=dt)
-        o, lse = wv.wave_attn(plan, desc, t, cache, q, scale)
+        if splits is None:
+            o, lse = wv.wave_attn(plan, desc, t, cache, q, scale)
+        else:
+            o, lse = wv.wave_attn_splitkv(plan, desc, t, cache, q, scale, num_splits=splits)
         torch.cuda.synchronize()
         o = o.float().cpu().numpy()
         lse = lse.cpu().numpy()
@@ -92,8 +97,8 @@ def gpu_rollout(plan, inputs, device, scale, src_dtype="fp32", poison=True, pert
     return outs
 
 
-def oracle_rollout(B, K, policy, H, L, cond, inputs, scale, rows=None, heads=None, want=None):
-    p = op.Params(B, K, policy, op.SERIAL, H, L, cond)
+def oracle_rollout(B, K, policy, H, L, cond, inputs, scale, rows=None, heads=None, want=None, query_len=0):
+    p = op.Params(B, K, policy, op.SERIAL, H, L, cond, query_len)
     return rollout(p, op.oracle_plan(p), inputs.q64, inputs.kv64, scale, rows=rows, heads=heads,
                    want=want)
 

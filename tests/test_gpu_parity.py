@@ -215,3 +215,84 @@ def test_long_video_capped_history_sampled(gpu_device):
         o, lse = got[key]
         s = compare(o[rows][:, heads], lse[heads][:, rows], o_ref[:, heads], lse_ref[heads], f"node {key}")
         log(f"  node {key}: {s}")
+
+
+SPLIT_GRID = [
+    # policy, H, cond, L, query_len, heads, hd, splits
+    (wi.PROGRESSIVE, -1, 0, 300, 0, 2, 128, 3),
+    (wi.SAME_LEVEL, -1, 70, 300, 64, 2, 128, 0),
+    (wi.CLEAN, -1, 0, 129, 1, 3, 64, 7),
+    (wi.PROGRESSIVE, 2, 33, 520, 100, 1, 128, 64),
+    (wi.SAME_LEVEL, 0, 0, 64, 0, 2, 64, 1),
+]
+
+
+@pytest.mark.parametrize("policy,H,cond,L,qlen,heads,hd,splits", SPLIT_GRID)
+def test_splitkv_grid_parity(gpu_device, policy, H, cond, L, qlen, heads, hd, splits):
+    """Split-KV attention (decode-shaped when query_len < chunk_len) against the oracle."""
+    B, K = 5, 3
+    log(f"splitkv policy={policy} H={H} cond={cond} L={L} qlen={qlen} heads={heads} hd={hd} splits={splits}")
+    plan = wv.wave_plan(B=B, K=K, policy=policy, sched=wv.WAVE, chunk_len=L, cond_len=cond, history_cap=H,
+                        query_len=qlen)
+    inp = HostInputs(200 + L, heads, hd, L, cond, bf16=True, query_len=qlen)
+    scale = 1.0 / np.sqrt(hd)
+    got = gpu_rollout(plan, inp, gpu_device, scale, src_dtype="bf16", splits=splits)
+    ref = oracle_rollout(B, K, policy, H, L, cond, inp, scale, query_len=qlen)
+    assert set(got) == set(ref)
+    for key in ref:
+        compare(got[key][0], got[key][1], ref[key][0], ref[key][1], f"node {key}")
+
+
+def test_streamer_audio_decode_splitkv(gpu_device):
+    """Decode-shaped Wan-Streamer round: the 64 audio rows of each chunk in round 7
+    (U(6,1) over 23,352 keys, U(7,2) over 26,688 keys) with split-KV, 8 heads
+    checked, against the oracle and against the unsplit kernel."""
+    import torch
+    w = wi.WORKLOADS[5]
+    qlen, t_meas, heads = 64, 7, list(range(0, 40, 5))
+    log(f"{w.name}: audio decode round {t_meas}, split-KV")
+    plan = wv.wave_plan(B=w.B, K=w.K, policy=wi.SAME_LEVEL, sched=wv.WAVE, chunk_len=w.chunk_len,
+                        cond_len=w.cond_len, query_len=qlen)
+    desc = plan.upload(gpu_device)
+    cache = wv.KVCache(plan.num_phys_slots, w.heads, w.head_dim, plan.lpad(), gpu_device, fill=float("nan"))
+    dev = {}
+
+    def kv_dev(c, lv):
+        if (c, lv) not in dev:
+            dev[(c, lv)] = (wi.device_tensor(w, 0, c, lv, "k", gpu_device, wi.SAME_LEVEL),
+                            wi.device_tensor(w, 0, c, lv, "v", gpu_device, wi.SAME_LEVEL))
+        return dev[(c, lv)]
+
+    for t in range(t_meas + 1):
+        ws = plan.round_writes(t).tolist()
+        wv.kv_write(plan, desc, t, cache, torch.cat([kv_dev(c, lv)[0] for (c, lv, _, _) in ws]),
+                    torch.cat([kv_dev(c, lv)[1] for (c, lv, _, _) in ws]))
+    nodes = plan.round_nodes(t_meas).tolist()
+    # the audio tokens are the last 64 of each chunk's 2824
+    qs = {(n[0], n[1]): wi.device_tensor(w, 0, n[0], n[1], "q", gpu_device, wi.SAME_LEVEL)[-qlen:].contiguous()
+          for n in nodes}
+    q = torch.cat([qs[(n[0], n[1])] for n in nodes])
+    o_s, lse_s = wv.wave_attn_splitkv(plan, desc, t_meas, cache, q, w.scale, num_splits=0)
+    o_f, lse_f = wv.wave_attn(plan, desc, t_meas, cache, q, w.scale)
+    torch.cuda.synchronize()
+    o_s, lse_s = o_s.float().cpu().numpy(), lse_s.cpu().numpy()
+    o_f, lse_f = o_f.float().cpu().numpy(), lse_f.cpu().numpy()
+    assert np.max(np.abs(o_s - o_f)) < 1e-2 and np.max(np.abs(lse_s - lse_f)) < 1e-4
+
+    class DevInputs:
+        def q64(self, c, lv):
+            return qs[(c, lv)].float().cpu().numpy().astype(np.float64)
+
+        def kv64(self, c, lv):
+            k, v = kv_dev(c, lv)
+            return k.float().cpu().numpy().astype(np.float64), v.float().cpu().numpy().astype(np.float64)
+
+    want = {(n[0], n[1]) for n in nodes}
+    ref = oracle_rollout(w.B, w.K, wi.SAME_LEVEL, w.history_cap, w.chunk_len, w.cond_len, DevInputs(), w.scale,
+                         heads=heads, want=want, query_len=qlen)
+    for n in nodes:
+        key = (n[0], n[1])
+        a, b = n[4], n[4] + n[5]
+        s = compare(o_s[a:b][:, heads], lse_s[heads][:, a:b], ref[key][0][:, heads], ref[key][1][heads],
+                    f"node {key}")
+        log(f"  node {key}: {s}")

@@ -19,9 +19,9 @@ from wave_inputs import WORKLOADS
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def native(B, K, policy, sched, H=-1, L=16, cond=0, q_tile=0):
+def native(B, K, policy, sched, H=-1, L=16, cond=0, q_tile=0, query_len=0):
     return wv.wave_plan(B=B, K=K, policy=policy, sched=sched, history_cap=H, chunk_len=L,
-                        cond_len=cond, q_tile=q_tile)
+                        cond_len=cond, q_tile=q_tile, query_len=query_len)
 
 
 def assert_same(pn, po):
@@ -58,6 +58,21 @@ def test_planner_matches_oracle_workloads(key):
             pn = native(w.B, w.K, pol, sch, w.history_cap, w.chunk_len, w.cond_len)
             po = op.oracle_plan(op.Params(w.B, w.K, pol, sch, w.history_cap, w.chunk_len, w.cond_len))
             assert_same(pn, po)
+
+
+@pytest.mark.parametrize("query_len", [1, 64, 100, 300])
+@pytest.mark.parametrize("pol", [op.CLEAN, op.SAME_LEVEL, op.PROGRESSIVE])
+def test_planner_query_len_matches_oracle(query_len, pol):
+    """Short query chunks (the decode-shaped case) change only row offsets."""
+    pn = native(6, 3, pol, op.WAVE, -1, 200, 33, query_len=query_len)
+    po = op.oracle_plan(op.Params(6, 3, pol, op.WAVE, -1, 200, 33, query_len))
+    assert_same(pn, po)
+    assert (pn.nodes[:, 5] == query_len).all()
+    for t in range(pn.num_rounds):
+        nb, ne = pn.round_node_begin[t], pn.round_node_begin[t + 1]
+        assert pn.round_q_rows[t] == query_len * (ne - nb)
+        items = pn.work[pn.round_work_begin[t]:pn.round_work_begin[t + 1]]
+        assert int(items[:, 2].sum()) == query_len * (ne - nb)
 
 
 def test_workload_capacities_and_rounds():
@@ -172,6 +187,20 @@ def test_device_calls_validate_before_launch():
     pn128 = native(4, 2, op.PROGRESSIVE, op.WAVE, -1, 128, 0, q_tile=128)
     assert lib.wave_attn(pn128.handle, fake, 0, C.byref(cache), fake, 0, 128, fake, None, 0.1,
                          stream) == _lib.WAVE_ERR_UNSUPPORTED
+
+    # split-KV: workspace checks
+    def split(ws=fake, nbytes=1 << 30, splits=2):
+        return lib.wave_attn_splitkv(pn.handle, fake, 0, C.byref(cache), fake, 0, 128, fake, None, 0.1,
+                                     splits, ws, nbytes, stream)
+
+    assert split(ws=None) == _lib.WAVE_ERR_INVALID_ARG
+    assert split(ws=C.c_void_p(0x10010)) == _lib.WAVE_ERR_INVALID_ARG  # not 256-byte aligned
+    assert split(nbytes=16) == _lib.WAVE_ERR_CAPACITY
+    assert split(splits=-1) == _lib.WAVE_ERR_INVALID_ARG
+    b, s = C.c_size_t(), C.c_int32()
+    assert lib.wave_attn_splitkv_workspace(pn.handle, 0, 2, 64, 3, C.byref(b), C.byref(s)) == 0
+    assert s.value == 3 and b.value >= 3 * 128 * 2 * 64 * 4 + 3 * 2 * 128 * 4
+    assert lib.wave_attn_splitkv_workspace(pn.handle, 9, 2, 64, 3, C.byref(b), C.byref(s)) != 0
 
     def kvw(round_=0, src=fake, dt=0, stride=128):
         return lib.kv_write(pn.handle, fake, round_, C.byref(cache), src, src, dt, stride, stream)

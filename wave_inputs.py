@@ -49,6 +49,7 @@ class Workload:
     sigma: float = 1.0
     host_fp32: bool = False  # draw on host as float32 (tiny case)
     round: int = -1          # single measured round, -1 = whole rollout
+    query_len: int = 0       # query rows per node, 0 = chunk_len (fewer: decode-shaped)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -71,6 +72,11 @@ WORKLOADS = {
     5: Workload(5, "wan-streamer-640x368-B8-K2-same-level-cond512-audio64", B=8, K=2,
                 policies=(SAME_LEVEL,), chunk_len=2760 + 64, heads=40, head_dim=128,
                 cond_len=512, round=7),
+    # Decode-shaped: only the 64 audio tokens of each chunk query (the audio
+    # latents follow the 2760 video tokens of the chunk).
+    6: Workload(6, "wan-streamer-640x368-audio-decode-64rows-round7", B=8, K=2,
+                policies=(SAME_LEVEL,), chunk_len=2760 + 64, heads=40, head_dim=128,
+                cond_len=512, round=7, query_len=64),
 }
 
 _MASK64 = (1 << 64) - 1
