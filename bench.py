@@ -11,6 +11,10 @@ tokens per 3-latent-frame chunk, 7 chunks), K=4 levels, progressive history,
 pipelined round 6: R(2), U(3,1), U(4,2), U(5,3), U(6,4) over 32,760 keys.
 
 Prints ONE JSON line on stdout.  Extra flags:
+  --rollout              whole rollouts instead of one round: workload 3 (7 chunks, K=5,
+                         30 layers, clean / same-level / progressive) or 4 (28 chunks, K=4,
+                         history cap 6); every (round, layer) runs kv_write + wave_attn, each
+                         pair timed with events after its inputs are generated
   --workload {2,4,5,6}   2 (default), 4 = long video steady round, 5 = Wan-Streamer round,
                          6 = Wan-Streamer audio decode (64 query rows per chunk, split-KV)
   --no-cpu-baseline      skip the CPU oracle timing
@@ -115,6 +119,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=768,
                     help="query rows per node for the CPU oracle (bounded sample, ~10-30 s of CPU work)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--rollout", action="store_true")
+    ap.add_argument("--layers", type=int, default=0, help="rollout layers (0 = the workload's)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -127,6 +133,9 @@ def main():
     import wave_inputs as wi
 
     device = torch.device("cuda:0")
+    if args.rollout:
+        rollout_bench(args, device)
+        return
     w = wi.WORKLOADS[args.workload]
     policy = w.policies[0]
     t_meas = w.round if w.round >= 0 else 16
@@ -285,6 +294,75 @@ def main():
     if copy_ms is not None:
         out["copy_1gib_ms"] = round(copy_ms, 4)
     print(json.dumps(out), flush=True)
+
+
+def rollout_bench(args, device):
+    """Whole pipelined rollouts: every round of every layer, kv_write then wave_attn."""
+    import torch
+    import block_causal_attention_wave_amd as wv
+    import wave_inputs as wi
+    key = args.workload if args.workload in (3, 4) else 3
+    w = wi.WORKLOADS[key]
+    layers = args.layers or w.layers
+    stream = torch.cuda.Stream()
+    results = []
+    for policy in w.policies:
+        plan = wv.wave_plan(B=w.B, K=w.K, policy=policy, sched=wv.WAVE, chunk_len=w.chunk_len,
+                            cond_len=w.cond_len, history_cap=w.history_cap)
+        desc = plan.upload(device)
+        caches = [wv.KVCache(plan.num_phys_slots, w.heads, w.head_dim, plan.lpad(), device, fill=float("nan"))
+                  for _ in range(layers)]
+        round_ms = np.zeros(plan.num_rounds)
+        attn_ms = np.zeros(plan.num_rounds)
+        flops = 0.0
+        finite = True
+        with torch.cuda.stream(stream):
+            for t in range(plan.num_rounds):
+                rows = int(plan.round_q_rows[t])
+                o = torch.empty((rows, w.heads, w.head_dim), dtype=torch.bfloat16, device=device)
+                lse = torch.empty((w.heads, rows), dtype=torch.float32, device=device)
+                flops += algorithmic_flops(plan, t, w.heads, w.head_dim) * layers
+                for layer in range(layers):
+                    ws = plan.round_writes(t).tolist()
+                    k_src = torch.cat([wi.device_tensor(w, layer, c, lv, "k", device, policy) for (c, lv, _, _) in ws])
+                    v_src = torch.cat([wi.device_tensor(w, layer, c, lv, "v", device, policy) for (c, lv, _, _) in ws])
+                    q = torch.cat([wi.device_tensor(w, layer, n[0], n[1], "q", device, policy)
+                                   for n in plan.round_nodes(t).tolist()])
+                    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                    stream.wait_stream(torch.cuda.default_stream(device))
+                    e0.record(stream)
+                    wv.kv_write(plan, desc, t, caches[layer], k_src, v_src, stream=stream)
+                    e1.record(stream)
+                    wv.wave_attn(plan, desc, t, caches[layer], q, w.scale, o=o, lse=lse, stream=stream)
+                    e2.record(stream)
+                    e2.synchronize()
+                    round_ms[t] += e0.elapsed_time(e2)
+                    attn_ms[t] += e1.elapsed_time(e2)
+                    finite = finite and bool(torch.isfinite(lse).all())
+        del caches
+        torch.cuda.empty_cache()
+        total = float(round_ms.sum())
+        # steady rounds: every level in flight (and, with a history cap, a full window)
+        first = w.K + (w.history_cap if w.history_cap >= 0 else 0)
+        steady = round_ms[first:w.B] if w.B > first else round_ms
+        res = {
+            "policy": wi.POLICY_NAMES[policy], "layers": layers, "rounds": plan.num_rounds,
+            "total_ms": round(total, 3), "ms_per_round": round(total / plan.num_rounds, 3),
+            "ms_per_chunk": round(total / w.B, 3), "tflop": round(flops / 1e12, 2),
+            "tflops": round(flops / (float(attn_ms.sum()) * 1e-3) / 1e12, 1),
+            "steady_round_ms": {"median": round(float(np.median(steady)), 3),
+                                "p10": round(float(np.percentile(steady, 10)), 3),
+                                "p90": round(float(np.percentile(steady, 90)), 3)},
+            "finite": finite,
+        }
+        eprint(f"[rollout] {w.name} {res['policy']}: {plan.num_rounds} rounds x {layers} layers, "
+               f"{total:.1f} ms total, {res['ms_per_round']:.2f} ms/round, {res['ms_per_chunk']:.2f} ms/chunk, "
+               f"{res['tflops']:.0f} TFLOP/s (attention), steady round median {res['steady_round_ms']['median']} ms")
+        results.append(res)
+    print(json.dumps({"metric": "wave rollout ms per round / per chunk + attention TFLOP/s", "workload": w.name,
+                      "unit": "ms", "n_gpus": 1, "dtype": "bf16", "data": "synthetic",
+                      "timing": "sum of per-(round, layer) kv_write + wave_attn event times",
+                      "results": results}), flush=True)
 
 
 def cpu_baseline(w, plan, t_meas, nodes, policy, layer, device, rows_per_node):
