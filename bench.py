@@ -114,7 +114,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, choices=(2, 4, 5, 6))
+    ap.add_argument("--workload", type=int, default=2, choices=(2, 3, 4, 5, 6))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=768,
                     help="query rows per node for the CPU oracle (bounded sample, ~10-30 s of CPU work)")
