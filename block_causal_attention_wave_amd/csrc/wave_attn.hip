@@ -24,10 +24,12 @@
 //     softmax registers (bf16), no data movement.
 // Online softmax in fp32: exp2 with the scale folded into one FMA, deferred
 // 1/l normalisation (FlashAttention-2), and a lazily raised reference: the
-// row max is only moved (rescaling O and l) when a block's scores exceed it
-// by more than 2^8, so the common block does no O rescale at all.
-// Scores of the next 32-key block are computed while the current block's
-// probabilities are formed, so MFMA and VALU work of one wave can overlap;
+// first block sets it to the exact row max, and it only moves again (with an
+// O and l rescale) when a block's probabilities, formed against it, sum to
+// more than 2^8 in some lane.  The common block computes no row max at all.
+// Each 32-key step issues the next block's scores and the previous block's
+// P.V product on the matrix cores and forms the current block's
+// probabilities on the vector ALUs, interleaved in one instruction stream;
 // with two waves per SIMD the hardware interleaves them as well.
 #include <hip/hip_runtime.h>
 
@@ -57,7 +59,7 @@ struct Cfg {
   static constexpr int KBYTES = kKT * KROW;
   static constexpr int VROW = kKT * 2;  // bytes per V^T row in LDS
   static constexpr int VBYTES = HD * VROW;
-  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int VBASE = 4 * KBYTES;  // K tiles of all stages, then V^T tiles
   static constexpr int NC = HD / 16;  // k-steps of Q.K^T
   static constexpr int ND = HD / 32;  // d blocks of O^T
   static constexpr int KLOADS = KBYTES / (THREADS * 16);
@@ -128,18 +130,20 @@ __device__ __forceinline__ void load_lds16(uint32_t lds_addr, const char* base, 
 
 // Issue one thread's direct global->LDS loads of a 64-key K tile (rows
 // permuted, chunks swizzled) and the matching V^T tile.  kt / vt point at the
-// tile's first key of the slot; wv is the (wave-uniform) wave index.
+// tile's first key of the slot; wv is the (wave-uniform) wave index.  `stage`
+// is the stage's K tile; its V^T tile sits VBASE bytes further.
 template <int HD, int W, int QB>
 __device__ __forceinline__ void issue_tile(char* stage, const char* kt, const char* vt,
                                            const TileOffsets<HD, W, QB>& off, int wv) {
   using C = Cfg<HD, W, QB>;
-  const uint32_t sbase = (uint32_t)(uintptr_t)stage;
+  const uint32_t kbase = (uint32_t)(uintptr_t)stage;
+  const uint32_t vbase = kbase + C::VBASE;
 #pragma unroll
   for (int n = 0; n < C::KLOADS; ++n)
-    load_lds16(sbase + (wv * C::KLOADS + n) * 1024, kt, off.k[n]);
+    load_lds16(kbase + (wv * C::KLOADS + n) * 1024, kt, off.k[n]);
 #pragma unroll
   for (int n = 0; n < C::VLOADS; ++n)
-    load_lds16(sbase + C::KBYTES + (wv * C::VLOADS + n) * 1024, vt, off.v[n]);
+    load_lds16(vbase + (wv * C::VLOADS + n) * 1024, vt, off.v[n]);
 }
 
 // Row max / sum across the two half-waves (lanes l and l^32 hold the same query).
@@ -207,25 +211,31 @@ __device__ __forceinline__ float block_rowmax(const f32x16& s) {
 // relative on short rows).
 template <int QB>
 __device__ __forceinline__ void softmax_block(const f32x16 (&s)[QB], float c2, const float (&mref)[QB],
-                                              bf16x8 (&pop)[QB][2], float (&l)[QB]) {
+                                              bf16x8 (&pop)[QB][2], float (&bsum)[QB]) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+  for (int qb = 0; qb < QB; ++qb) {
+    float sum0 = 0.0f, sum1 = 0.0f;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       bf16x8 pv;
-      float sum0 = 0.0f, sum1 = 0.0f;
 #pragma unroll
       for (int t = 0; t < 8; t += 2) {
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][8 * hh + t], c2, -mref[qb]));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][8 * hh + t + 1], c2, -mref[qb]));
-        sum0 += p0;
-        sum1 += p1;
+        if (hh == 0 && t == 0) {
+          sum0 = p0;
+          sum1 = p1;
+        } else {
+          sum0 += p0;
+          sum1 += p1;
+        }
         pv[t] = (__bf16)p0;
         pv[t + 1] = (__bf16)p1;
       }
-      l[qb] += sum0 + sum1;
       pop[qb][hh] = pv;
     }
+    bsum[qb] = sum0 + sum1;
+  }
 }
 
 // O^T += V^T(block kb) . P^T
@@ -246,10 +256,12 @@ __device__ __forceinline__ void pv_block(const char* vs, int kb, const bf16x8 (&
   }
 }
 
-// A block whose scores exceed the softmax reference by more than this many
-// powers of two raises the reference (rescaling O and l); below that the
-// stale reference is kept: p <= 2^8 is exact enough in fp32 and bf16.
+// A block whose probabilities against the softmax reference sum to more than
+// 2^kRescaleLog2 in some lane raises the reference (rescaling O and l);
+// otherwise the stale reference is kept: each p <= 2^8 is exact enough in
+// fp32 and bf16 and far from overflow in the fp32 accumulators.
 constexpr float kRescaleLog2 = 8.0f;
+constexpr float kRescaleSum = 256.0f;  // 2^kRescaleLog2
 
 // Walks the gather list tile by tile, keeping the current slot's index and
 // length in scalar registers.
@@ -295,6 +307,39 @@ struct Walker {
   }
 };
 
+// The loader's walk: the current tile's K and V^T addresses in scalar
+// registers, stepped by one tile inside a slot and recomputed from the slot
+// index when the walk enters the next slot.
+template <int HD>
+struct TileFeed {
+  Walker w;
+  const char* k0;  // K of this head in cache slot 0
+  const char* v0;  // V^T of this head in cache slot 0
+  int64_t slot_bytes;
+  const char* kt = nullptr;
+  const char* vt = nullptr;
+  __device__ __forceinline__ TileFeed(const int* c, int n, const char* k, const char* v, int64_t sb, int first)
+      : w(c, n), k0(k), v0(v), slot_bytes(sb) {
+    w.skip(first);
+    point();
+  }
+  __device__ __forceinline__ void point() {
+    const int64_t off = (int64_t)w.phys() * slot_bytes;
+    kt = k0 + off + (int64_t)w.key0() * (HD * 2);
+    vt = v0 + off + (int64_t)w.key0() * 2;
+  }
+  __device__ __forceinline__ void next() {
+    if ((w.t + 1) * kKT >= w.len_) {
+      w.next();
+      point();
+    } else {
+      ++w.t;
+      kt += kKT * HD * 2;
+      vt += kKT * 2;
+    }
+  }
+};
+
 // SPLIT = false: one workgroup per (work item, head) over the node's whole
 // gather list; writes bf16 O and the LSE.
 // SPLIT = true (split-KV, for short query chunks against long contexts):
@@ -307,7 +352,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * W, 64 * W), amdgpu_wa
 void wave_attn_kernel(AttnArgs a) {
   using C = Cfg<HD, W, QB>;
   constexpr int NS = kStages;
-  __shared__ __attribute__((aligned(1024))) char lds[NS * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds[NS * (C::KBYTES + C::VBYTES)];
   __shared__ int ctx_lds[2 * kMaxCtx];
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -335,6 +380,10 @@ void wave_attn_kernel(AttnArgs a) {
   // The gather list goes to LDS once, so that walking it inside the tile
   // loop never waits on the vector-memory counter the K/V prefetch uses.
   for (int e = threadIdx.x; e < 2 * ctx_count; e += C::THREADS) ctx_lds[e] = ctx_g[e];
+  // The V^T tile of ring stage NS-1 (where tile -1 would sit) starts as
+  // zeros: the first pipeline step multiplies it by a zero P.
+  for (int i = threadIdx.x; i < C::VBYTES / 16; i += C::THREADS)
+    reinterpret_cast<f32x4*>(lds + C::VBASE + (kStages - 1) * C::VBYTES)[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   __syncthreads();
   int total_tiles = 0;
   for (int e = 0; e < ctx_count; ++e) total_tiles += (ctx_lds[2 * e + 1] + kKT - 1) / kKT;
@@ -351,7 +400,7 @@ void wave_attn_kernel(AttnArgs a) {
       return;
     }
   }
-  const bool active = !SPLIT || wv * QB * 32 < q_rows;  // wave-uniform
+  const bool active = !SPLIT || wv_u * QB * 32 < q_rows;  // wave-uniform (scalar compare)
 
   // Q fragments (B operand of S^T): lane holds query (lane & 31) of block qb,
   // dims 16c + 8*(lane>>5) .. +7.
@@ -394,14 +443,11 @@ void wave_attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) l[qb] = 0.0f;
 
-  Walker ld(ctx_lds, ctx_count);
-  ld.skip(first_tile);
+  TileFeed<HD> ld(ctx_lds, ctx_count, reinterpret_cast<const char*>(kcache),
+                  reinterpret_cast<const char*>(vcache), slot_elems * 2, first_tile);
   const TileOffsets<HD, W, QB> toff(lpad, wv, lane);
   auto issue = [&](int stage) {
-    const int64_t slot = (int64_t)ld.phys() * slot_elems;
-    const char* kt = reinterpret_cast<const char*>(kcache + slot + (int64_t)ld.key0() * HD);
-    const char* vt = reinterpret_cast<const char*>(vcache + slot + ld.key0());
-    issue_tile<HD, W, QB>(lds + stage * C::STAGE, kt, vt, toff, wv_u);
+    issue_tile<HD, W, QB>(lds + stage * C::KBYTES, ld.kt, ld.vt, toff, wv_u);
     ld.next();
   };
   constexpr int kWaitExp = (0x7 << 4) | (0xF << 8);
@@ -433,20 +479,25 @@ void wave_attn_kernel(AttnArgs a) {
     for (int qb = 0; qb < QB; ++qb) mref[qb] = c2 * block_rowmax(sa[qb]);
   }
 
-  // Raise the reference if the freshly computed block exceeds it by more
-  // than 2^kRescaleLog2 (wave-uniform branch; rare after the first blocks).
-  auto check = [&](const f32x16 (&snew)[QB]) {
-    float over[QB];
-    bool raise = false;
+  // A block's probabilities were formed against the current reference; if
+  // some lane's sum over its 16 keys exceeds 2^kRescaleLog2 (a score above the
+  // reference by more than that, or an overflow to inf), the block is redone:
+  // its scores are recomputed from the K tile still in LDS, the reference is
+  // raised to the block's exact row max (rescaling O and l), and the
+  // probabilities are formed again.  Rare after the first block, which sets the
+  // reference exactly; otherwise the block's sums go straight into l.
+  auto settle = [&](float (&bsum)[QB], bf16x8 (&pop)[QB][2], const char* kst, int kb, int valid)
+      __attribute__((always_inline)) {
+    bool big = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      over[qb] = c2 * block_rowmax(snew[qb]) - mref[qb];
-      raise |= over[qb] > kRescaleLog2;
-    }
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+    for (int qb = 0; qb < QB; ++qb) big |= bsum[qb] > kRescaleSum;
+    if (__builtin_amdgcn_ballot_w64(big) != 0) {
+      f32x16 sr[QB];
+      qk_block<HD, QB>(kst, kb, qop, sr, lane);
+      if (valid < 32) mask_block<QB>(sr, valid, lane);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const float delta = fmaxf(over[qb], 0.0f);
+        const float delta = fmaxf(c2 * block_rowmax(sr[qb]) - mref[qb], 0.0f);
         const float alpha = __builtin_amdgcn_exp2f(-delta);
         mref[qb] += delta;
         l[qb] *= alpha;
@@ -455,46 +506,84 @@ void wave_attn_kernel(AttnArgs a) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) o[db][qb][i] *= alpha;
       }
+      softmax_block<QB>(sr, c2, mref, pop, bsum);
     }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l[qb] += bsum[qb];
   };
 
-  // One 64-key tile: block 0 (scores in sa) while block 1's scores go to sb,
-  // then block 1 while block 0 of the next tile goes to sa.  Only a slot's
-  // last tile is ragged and gets the tail mask.
-  // The ring stage of tile n is n % NS; the loop below is unrolled NS times
-  // so that it is a compile-time constant and every LDS operand address is a
-  // per-lane base plus an immediate offset.
-  auto tile = [&](int n, auto stage_tag) __attribute__((always_inline)) {
+  // Software pipeline over 32-key blocks: step j issues the scores of block
+  // j+1 and the P.V product of block j-1 on the matrix cores, then forms the
+  // probabilities of block j on the vector ALUs; the three are independent,
+  // so one wave's MFMA and VALU work overlap.  Block j's P waits in
+  // registers (pprev) until step j+1.  Each 64-key tile is two steps (block 0
+  // with scores in sa, block 1 with scores in sb); the ring stage of tile n is
+  // n % NS and the loop is unrolled NS tiles so that every LDS operand address
+  // is a per-lane base plus an immediate.
+  // The V^T region starts at 64 KiB, past the reach of an LDS instruction's
+  // immediate offset; hiding its start from the compiler makes it part of the
+  // per-lane base register, so the stage and block offsets stay immediates.
+  uint32_t vregion = C::VBASE;
+  asm volatile("" : "+s"(vregion));
+  bf16x8 pprev[QB][2];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pprev[qb][hh][i] = (__bf16)0.0f;
+  auto step = [&](int n, auto stage_tag, auto kb_tag, f32x16 (&scur)[QB], f32x16 (&snext)[QB])
+      __attribute__((always_inline)) {
     constexpr int ST = decltype(stage_tag)::value;
-    const char* st = lds + ST * C::STAGE;
+    constexpr int KB = decltype(kb_tag)::value;
+    constexpr int SP = (ST + NS - 1) % NS;  // stage of tile n-1
+    const char* kst = lds + ST * C::KBYTES;
+    const char* vst = lds + vregion + ST * C::VBYTES;
     const int valid = cur.valid();
+    const bool has_next = KB == 0 || n + 1 < total_tiles;
+    if constexpr (KB == 1) {
+      wait_tiles(min(total_tiles - 2 - n, NS - 3));
+      barrier();
+      if (n + NS - 1 < total_tiles) issue((ST + NS - 1) % NS);
+    }
     if (active) {
-      bf16x8 pop[QB][2];
-      qk_block<HD, QB>(st, 1, qop, sb, lane);
-      softmax_block<QB>(sa, c2, mref, pop, l);
-      pv_block<HD, QB>(st + C::KBYTES, 0, pop, o, lane);
-      if (valid < 64) mask_block<QB>(sb, valid - 32, lane);
-      check(sb);
+      // Without a next block the scores are formed from a stale stage and
+      // never used; for the first block of the walk, pprev and the V^T half
+      // it meets are zero.
+      qk_block<HD, QB>(lds + (KB == 0 ? ST : (ST + 1) % NS) * C::KBYTES, KB ^ 1, qop, snext, lane);
+      if constexpr (KB == 0) {
+        pv_block<HD, QB>(lds + vregion + SP * C::VBYTES, 1, pprev, o, lane);
+      } else {
+        pv_block<HD, QB>(vst, 0, pprev, o, lane);
+      }
+      float bsum[QB];
+      softmax_block<QB>(scur, c2, mref, pprev, bsum);
+      // Instruction order of the step: two LDS operand reads ahead, then
+      // (MFMA, 3 VALU, LDS read) groups.
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < 16 - 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+      settle(bsum, pprev, kst, KB, valid - 32 * KB);
     }
-    {
-      bf16x8 pop[QB][2];
-      const bool has_next = n + 1 < total_tiles;
-      if (has_next) {
-        wait_tiles(min(total_tiles - 2 - n, NS - 3));
-        barrier();
-        if (n + NS - 1 < total_tiles) issue((ST + NS - 1) % NS);
-        if (active) qk_block<HD, QB>(lds + ((ST + 1) % NS) * C::STAGE, 0, qop, sa, lane);
-      }
-      if (active) {
-        softmax_block<QB>(sb, c2, mref, pop, l);
-        pv_block<HD, QB>(st + C::KBYTES, 1, pop, o, lane);
-      }
+    if constexpr (KB == 0) {
+      if (active && valid < 64) mask_block<QB>(snext, valid - 32, lane);
+    } else {
       cur.next();
-      if (has_next && active) {
-        if (cur.valid() < 32) mask_block<QB>(sa, cur.valid(), lane);
-        check(sa);
-      }
+      if (has_next && active && cur.valid() < 32) mask_block<QB>(snext, cur.valid(), lane);
     }
+  };
+  auto tile = [&](int n, auto stage_tag) __attribute__((always_inline)) {
+    step(n, stage_tag, std::integral_constant<int, 0>{}, sa, sb);
+    step(n, stage_tag, std::integral_constant<int, 1>{}, sb, sa);
   };
 
   static_assert(NS == 4, "the tile loop below is unrolled for a 4-stage ring");
@@ -504,6 +593,8 @@ void wave_attn_kernel(AttnArgs a) {
     if (n + 2 < total_tiles) tile(n + 2, std::integral_constant<int, 2>{});
     if (n + 3 < total_tiles) tile(n + 3, std::integral_constant<int, 3>{});
   }
+  // P.V of the last block (block 1 of the last tile).
+  if (active) pv_block<HD, QB>(lds + vregion + ((total_tiles - 1) % NS) * C::VBYTES, 1, pprev, o, lane);
 
   // Epilogue: O = O^T / l, LSE = ln2 * (mref + log2 l).
   if (!active) return;

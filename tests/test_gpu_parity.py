@@ -296,3 +296,40 @@ def test_streamer_audio_decode_splitkv(gpu_device):
         s = compare(o_s[a:b][:, heads], lse_s[heads][:, a:b], ref[key][0][:, heads], ref[key][1][heads],
                     f"node {key}")
         log(f"  node {key}: {s}")
+
+
+class WideScoreInputs(HostInputs):
+    """Q and K scaled by `spread` (V left at unit scale): scaled scores have a
+    standard deviation of spread^2, so blocks late in a row's context exceed
+    the first block's maximum by tens to hundreds of powers of two.  This
+    drives the online softmax's reference-raising path, including
+    probabilities that overflow fp32 against the stale reference."""
+
+    def __init__(self, spread, *args, **kw):
+        super().__init__(*args, **kw)
+        self.spread = spread
+
+    def _get(self, chunk, level, which):
+        k = (chunk, level, which)
+        if k not in self._cache:
+            x = super()._get(chunk, level, which)
+            if which in ("q", "k"):
+                x = round_to_bf16(x * np.float32(self.spread)) if self.bf16 else x * np.float32(self.spread)
+            self._cache[k] = x
+        return self._cache[k]
+
+
+@pytest.mark.parametrize("spread,hd,splits", [(2.0, 128, None), (3.0, 64, None), (6.0, 128, None),
+                                              (10.0, 128, None), (6.0, 128, 5), (10.0, 64, 3)])
+def test_wide_score_range_parity(gpu_device, spread, hd, splits):
+    B, K, L, cond, heads = 5, 3, 300, 40, 2
+    log(f"wide scores spread={spread} hd={hd} splits={splits}")
+    plan = wv.wave_plan(B=B, K=K, policy=wi.PROGRESSIVE, sched=wv.WAVE, chunk_len=L, cond_len=cond)
+    inp = WideScoreInputs(spread, 300 + int(spread), heads, hd, L, cond, bf16=True)
+    scale = 1.0 / np.sqrt(hd)
+    got = gpu_rollout(plan, inp, gpu_device, scale, src_dtype="bf16", splits=splits)
+    ref = oracle_rollout(B, K, wi.PROGRESSIVE, -1, L, cond, inp, scale)
+    assert set(got) == set(ref)
+    for key in ref:
+        s = compare(got[key][0], got[key][1], ref[key][0], ref[key][1], f"node {key}")
+    log(f"  last node stats {s}")
