@@ -118,6 +118,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=768,
                     help="query rows per node for the CPU oracle (bounded sample, ~10-30 s of CPU work)")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="split-KV key ranges for decode-shaped rounds (0 = the library's choice)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--rollout", action="store_true")
     ap.add_argument("--layers", type=int, default=0, help="rollout layers (0 = the workload's)")
@@ -176,7 +178,7 @@ def main():
     workspace = None
     splits = 1
     if decode:
-        nbytes, splits = wv.splitkv_workspace_bytes(plan, t_meas, w.heads, w.head_dim, 0)
+        nbytes, splits = wv.splitkv_workspace_bytes(plan, t_meas, w.heads, w.head_dim, args.splits)
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
 
     def attn(stream):

@@ -429,6 +429,14 @@ void wave_attn_kernel(AttnArgs a) {
       qop[qb][c] = v;
     }
   }
+  // Let the Q loads land here, on every path.  Their uses sit under
+  // wave-uniform branches the compiler cannot see through, and it would
+  // otherwise wait for every outstanding load (tile prefetches included)
+  // before the first MFMA of each pipeline step.
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) asm volatile("" ::"v"(qop[qb][c]));
 
   f32x16 o[C::ND][QB];
 #pragma unroll
