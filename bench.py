@@ -120,6 +120,8 @@ def main():
                     help="query rows per node for the CPU oracle (bounded sample, ~10-30 s of CPU work)")
     ap.add_argument("--splits", type=int, default=0,
                     help="split-KV key ranges for decode-shaped rounds (0 = the library's choice)")
+    ap.add_argument("--no-balance", action="store_true",
+                    help="wave_attn without tail balancing (each node bitwise independent of the schedule)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--rollout", action="store_true")
     ap.add_argument("--layers", type=int, default=0, help="rollout layers (0 = the workload's)")
@@ -177,15 +179,23 @@ def main():
     attn_bytes = attention_bytes(plan, t_meas, w.heads, w.head_dim)
     workspace = None
     splits = 1
+    tail = (0, 1)
     if decode:
         nbytes, splits = wv.splitkv_workspace_bytes(plan, t_meas, w.heads, w.head_dim, args.splits)
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    elif not args.no_balance:
+        # tail balancing: the library's choice of trailing work items to cut
+        nbytes, tail_items, tail_splits = wv.attn_workspace(plan, t_meas, w.heads, w.head_dim)
+        tail = (tail_items, tail_splits)
+        if nbytes > 0:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
 
     def attn(stream):
         if decode:
             return wv.wave_attn_splitkv(plan, desc, t_meas, cache, q, w.scale, num_splits=splits,
                                         workspace=workspace, o=o, lse=lse, stream=stream)
-        return wv.wave_attn(plan, desc, t_meas, cache, q, w.scale, o=o, lse=lse, stream=stream)
+        return wv.wave_attn(plan, desc, t_meas, cache, q, w.scale, o=o, lse=lse, stream=stream,
+                            balance=not args.no_balance, workspace=workspace)
 
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
@@ -266,6 +276,8 @@ def main():
             "heads": w.heads, "head_dim": w.head_dim, "history_cap": w.history_cap,
             "nodes_in_round": len(nodes), "query_rows": rows, "query_rows_per_node": qlen,
             "splitkv_splits": splits if decode else None,
+            "tail_cut_items": None if decode else tail[0],
+            "tail_cut_splits": None if decode else tail[1],
             "algorithmic_tflop": round(flops / 1e12, 4),
         },
         "attn_ms": round(attn_avg, 4),
@@ -316,6 +328,8 @@ def rollout_bench(args, device):
                   for _ in range(layers)]
         round_ms = np.zeros(plan.num_rounds)
         attn_ms = np.zeros(plan.num_rounds)
+        ws_bytes = max(wv.attn_workspace(plan, t, w.heads, w.head_dim)[0] for t in range(plan.num_rounds))
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device)
         flops = 0.0
         finite = True
         with torch.cuda.stream(stream):
@@ -335,7 +349,8 @@ def rollout_bench(args, device):
                     e0.record(stream)
                     wv.kv_write(plan, desc, t, caches[layer], k_src, v_src, stream=stream)
                     e1.record(stream)
-                    wv.wave_attn(plan, desc, t, caches[layer], q, w.scale, o=o, lse=lse, stream=stream)
+                    wv.wave_attn(plan, desc, t, caches[layer], q, w.scale, o=o, lse=lse, stream=stream,
+                                 workspace=workspace)
                     e2.record(stream)
                     e2.synchronize()
                     round_ms[t] += e0.elapsed_time(e2)

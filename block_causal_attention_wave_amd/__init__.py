@@ -184,15 +184,40 @@ def _attn_outputs(plan, round, cache, q, o, lse, want_lse):
     return o, lse
 
 
+def attn_workspace(plan: Plan, round: int, heads: int, head_dim: int, compute_units: int = 0):
+    """(bytes, tail_items, tail_splits) of wave_attn's tail balancing for this round
+    (compute_units 0 = the current device's)."""
+    b = C.c_size_t()
+    m = C.c_int32()
+    s = C.c_int32()
+    _lib.check(_lib.load().wave_attn_workspace(plan.handle, round, heads, head_dim, compute_units,
+                                               C.byref(b), C.byref(m), C.byref(s)))
+    return b.value, m.value, s.value
+
+
 def wave_attn(plan: Plan, d_desc, round: int, cache: KVCache, q, scale: float, o=None, lse=None,
-              want_lse=True, stream=None):
-    """Attention of round `round`: q [rows, heads, d] (bf16 or fp32) -> (o bf16, lse fp32 [heads, rows])."""
+              want_lse=True, stream=None, balance=True, workspace=None):
+    """Attention of round `round`: q [rows, heads, d] (bf16 or fp32) -> (o bf16, lse fp32 [heads, rows]).
+
+    balance: cut the round's trailing work items into key ranges when that
+    shortens it (results then equal the unbalanced ones up to rounding); the
+    workspace (uint8 tensor of attn_workspace() bytes) is allocated here when
+    not given.  balance=False keeps each node's result bitwise independent of
+    the schedule."""
+    import torch
     o, lse = _attn_outputs(plan, round, cache, q, o, lse, want_lse)
+    ws_ptr, ws_bytes = 0, 0
+    if balance:
+        nbytes, _, _ = attn_workspace(plan, round, cache.heads, cache.head_dim)
+        if workspace is None and nbytes > 0:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        if workspace is not None:
+            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     _lib.check(_lib.load().wave_attn(plan.handle, C.c_void_p(d_desc.data_ptr()), round, C.byref(cache.c),
                                      C.c_void_p(q.data_ptr()), _dtype_code(q), q.stride(0),
                                      C.c_void_p(o.data_ptr()),
                                      C.c_void_p(lse.data_ptr() if lse is not None else 0),
-                                     float(scale), _stream_ptr(stream)))
+                                     float(scale), C.c_void_p(ws_ptr), ws_bytes, _stream_ptr(stream)))
     return o, lse
 
 

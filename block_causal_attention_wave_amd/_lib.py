@@ -23,7 +23,7 @@ WAVE_Q_TILE = 256
 WAVE_KEY_TILE = 64
 
 EXPORTS = ("wave_plan", "wave_plan_view_get", "wave_plan_desc_size", "wave_plan_desc_pack",
-           "wave_plan_destroy", "kv_write", "wave_attn", "wave_attn_splitkv_workspace",
+           "wave_plan_destroy", "kv_write", "wave_attn_workspace", "wave_attn", "wave_attn_splitkv_workspace",
            "wave_attn_splitkv", "wave_last_error")
 
 
@@ -94,9 +94,12 @@ def load() -> C.CDLL:
     lib.kv_write.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.POINTER(KvCache),
                              C.c_void_p, C.c_void_p, C.c_int32, C.c_int64, C.c_void_p]
     lib.kv_write.restype = C.c_int32
+    lib.wave_attn_workspace.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                        C.POINTER(C.c_size_t), C.POINTER(C.c_int32), C.POINTER(C.c_int32)]
+    lib.wave_attn_workspace.restype = C.c_int32
     lib.wave_attn.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.POINTER(KvCache),
                               C.c_void_p, C.c_int32, C.c_int64, C.c_void_p, C.c_void_p,
-                              C.c_float, C.c_void_p]
+                              C.c_float, C.c_void_p, C.c_size_t, C.c_void_p]
     lib.wave_attn.restype = C.c_int32
     lib.wave_attn_splitkv_workspace.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                                 C.POINTER(C.c_size_t), C.POINTER(C.c_int32)]

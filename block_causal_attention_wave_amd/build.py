@@ -26,6 +26,7 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
 
 SOURCES = [
     ("planner.cpp", False),
+    ("balance.cpp", False),
     ("abi.cpp", False),
     ("kv_write.hip", True),
     ("wave_attn.hip", True),

@@ -3,17 +3,24 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <new>
 #include <string>
 
+#include "balance.hpp"
 #include "kernels.hpp"
 #include "planner.hpp"
 #include "wave.h"
 
 struct wave_plan {
   wave::Plan p;
+  // tail-balancing choices, memoised per (round, heads, head_dim, compute units)
+  mutable std::mutex mu;
+  mutable std::map<std::array<int32_t, 4>, wave::TailSplit> tails;
 };
 
 namespace {
@@ -156,15 +163,21 @@ int32_t kv_write(const wave_plan_t* plan, const void* d_desc, int32_t round, con
 
 namespace {
 
-// Splits for split-KV attention: enough workgroups for about two per compute
-// unit, at most 64 splits.
-int32_t auto_splits(const wave::Plan& p, int32_t round, int32_t heads) {
+// Compute units of the current device (256 if it cannot be queried).
+int32_t device_cus() {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
     (void)hipGetLastError();
     cus = 256;
   }
+  return cus;
+}
+
+// Splits for split-KV attention: enough workgroups for about two per compute
+// unit, at most 64 splits.
+int32_t auto_splits(const wave::Plan& p, int32_t round, int32_t heads) {
+  const int32_t cus = device_cus();
   const int64_t items = static_cast<int64_t>(p.round_work_begin[round + 1] - p.round_work_begin[round]) * heads;
   if (items <= 0) return 1;
   int64_t s = (2 * static_cast<int64_t>(cus) + items - 1) / items;
@@ -172,6 +185,30 @@ int32_t auto_splits(const wave::Plan& p, int32_t round, int32_t heads) {
 }
 
 constexpr size_t kAlign = 256;
+
+wave::TailSplit tail_for(const wave_plan_t* plan, int32_t round, int32_t heads, int32_t head_dim, int32_t cus) {
+  const std::array<int32_t, 4> key{round, heads, head_dim, cus};
+  std::lock_guard<std::mutex> lock(plan->mu);
+  auto it = plan->tails.find(key);
+  if (it != plan->tails.end()) return it->second;
+  const wave::TailSplit t = wave::choose_tail_split(plan->p, round, heads, head_dim, cus);
+  plan->tails.emplace(key, t);
+  return t;
+}
+
+// Workspace of tail balancing: fp32 O [splits][items*256][heads][d], then
+// (256-byte aligned) fp32 LSE [splits][heads][items*256].
+size_t tail_bytes(const wave::TailSplit& t, int32_t heads, int32_t head_dim, size_t* lse_offset) {
+  if (t.items == 0) {
+    if (lse_offset) *lse_offset = 0;
+    return 0;
+  }
+  const size_t prows = static_cast<size_t>(t.items) * WAVE_Q_TILE;
+  const size_t o_bytes = static_cast<size_t>(t.splits) * prows * heads * head_dim * sizeof(float);
+  const size_t off = (o_bytes + kAlign - 1) / kAlign * kAlign;
+  if (lse_offset) *lse_offset = off;
+  return off + static_cast<size_t>(t.splits) * heads * prows * sizeof(float);
+}
 
 size_t splitkv_bytes(const wave::Plan& p, int32_t round, int32_t heads, int32_t head_dim, int32_t splits,
                      size_t* lse_offset) {
@@ -225,6 +262,9 @@ int32_t attn_common(const wave_plan_t* plan, const void* d_desc, int32_t round, 
   a.lse_stride = p.round_q_rows[round];
   a.scale_log2e = scale * 1.4426950408889634f;
   a.num_splits = 1;
+  a.num_direct = a.num_work;
+  a.tail_splits = 1;
+  a.part_rows = 0;
   return WAVE_OK;
 }
 
@@ -232,13 +272,47 @@ int32_t attn_common(const wave_plan_t* plan, const void* d_desc, int32_t round, 
 
 extern "C" {
 
+int32_t wave_attn_workspace(const wave_plan_t* plan, int32_t round, int32_t heads, int32_t head_dim,
+                            int32_t compute_units, size_t* bytes, int32_t* tail_items, int32_t* tail_splits) {
+  if (!plan || !bytes) return set_error(WAVE_ERR_INVALID_ARG, "wave_attn_workspace: null argument");
+  const wave::Plan& p = plan->p;
+  if (round < 0 || round >= p.num_rounds())
+    return set_error(WAVE_ERR_INVALID_ARG, "wave_attn_workspace: round out of range");
+  if (heads < 1 || heads > 65535 || (head_dim != 64 && head_dim != 128) || compute_units < 0)
+    return set_error(WAVE_ERR_INVALID_ARG, "wave_attn_workspace: bad heads, head_dim or compute_units");
+  const wave::TailSplit t =
+      tail_for(plan, round, heads, head_dim, compute_units == 0 ? device_cus() : compute_units);
+  *bytes = tail_bytes(t, heads, head_dim, nullptr);
+  if (tail_items) *tail_items = t.items;
+  if (tail_splits) *tail_splits = t.splits;
+  return ok();
+}
+
 int32_t wave_attn(const wave_plan_t* plan, const void* d_desc, int32_t round, const wave_kv_cache* cache,
                   const void* q, int32_t q_dtype, int64_t q_row_stride, void* o, float* lse, float scale,
-                  void* stream) {
+                  void* workspace, size_t workspace_bytes, void* stream) {
   wave::AttnArgs a;
   const int32_t rc = attn_common(plan, d_desc, round, cache, q, q_dtype, q_row_stride, o, lse, scale,
                                  "wave_attn", a);
   if (rc != WAVE_OK) return rc;
+  if (workspace) {
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+      return set_error(WAVE_ERR_INVALID_ARG, "wave_attn: workspace must be 256-byte aligned");
+    const wave::TailSplit t = tail_for(plan, round, cache->heads, cache->head_dim, device_cus());
+    size_t lse_off = 0;
+    const size_t need = tail_bytes(t, cache->heads, cache->head_dim, &lse_off);
+    if (workspace_bytes < need)
+      return set_error(WAVE_ERR_CAPACITY, "wave_attn: workspace smaller than wave_attn_workspace()");
+    if (t.items > 0) {
+      if (static_cast<int64_t>(a.num_work) * cache->heads * t.splits > INT32_MAX)
+        return set_error(WAVE_ERR_UNSUPPORTED, "wave_attn: too many workgroups");
+      a.num_direct = a.num_work - t.items;
+      a.tail_splits = t.splits;
+      a.part_rows = t.items * WAVE_Q_TILE;
+      a.part_o = static_cast<float*>(workspace);
+      a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + lse_off);
+    }
+  }
   const hipError_t e = wave::launch_wave_attn(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return set_error(WAVE_ERR_HIP, std::string("wave_attn: ") + hipGetErrorString(e));
   return ok();
@@ -278,6 +352,7 @@ int32_t wave_attn_splitkv(const wave_plan_t* plan, const void* d_desc, int32_t r
   if (static_cast<int64_t>(a.num_work) * cache->heads * s > INT32_MAX)
     return set_error(WAVE_ERR_UNSUPPORTED, "wave_attn_splitkv: too many workgroups");
   a.num_splits = s;
+  a.part_rows = p.round_q_rows[round];
   a.part_o = static_cast<float*>(workspace);
   a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + lse_off);
   if (s == 1) {

@@ -39,9 +39,17 @@ struct AttnArgs {
   int32_t lse_stride;  // rows of the round (LSE is [heads][rows])
   float scale_log2e;   // scale * log2(e)
   // split-KV: > 1 splits each node's key tiles into that many contiguous
-  // ranges; partial results go to part_o (fp32 [splits][rows][heads][d]) and
-  // part_lse (fp32 [splits][heads][rows]) and are merged into o / lse.
+  // ranges; partial results go to part_o (fp32 [splits][part_rows][heads][d])
+  // and part_lse (fp32 [splits][heads][part_rows]) and are merged into o / lse.
+  // Partial row = the round row (part_rows = the round's rows).
   int32_t num_splits;
+  // Tail balancing (num_splits <= 1): items [0, num_direct) are processed
+  // whole; each later item is cut into tail_splits key ranges, with partial
+  // row = (item - num_direct) * 256 + row in the item (part_rows = the tail
+  // items times 256), merged afterwards.  num_direct = num_work: none.
+  int32_t num_direct;
+  int32_t tail_splits;
+  int32_t part_rows;
   float* part_o;
   float* part_lse;
 };

@@ -173,20 +173,41 @@ int32_t kv_write(const wave_plan_t* plan, const void* d_desc, int32_t round,
                  const wave_kv_cache* cache, const void* k_src, const void* v_src,
                  int32_t src_dtype, int64_t src_row_stride, void* stream);
 
+/* Workspace of wave_attn's tail balancing for round `round`, `heads` heads of
+ * `head_dim` on a device of `compute_units` compute units (0 = the current
+ * device).  wave_attn runs one workgroup per (work item, head) in the plan's
+ * work order, most key tiles first; when those workgroups do not divide
+ * evenly over the compute units, the last of them run on a part-empty chip.
+ * The library picks, from a simulation of that in-order dispatch, the number
+ * of trailing work items to cut into contiguous key-tile ranges (1 to 4
+ * pieces, merged by a second kernel as in wave_attn_splitkv).  *bytes = 0
+ * when no cut pays off.  tail_items, tail_splits (may be NULL) receive the
+ * choice.  The choice is memoised in the plan; this call is thread-safe. */
+int32_t wave_attn_workspace(const wave_plan_t* plan, int32_t round, int32_t heads,
+                            int32_t head_dim, int32_t compute_units, size_t* bytes,
+                            int32_t* tail_items, int32_t* tail_splits);
+
 /* Block-causal attention of every node of round `round`.
  *   q  : device [round_q_rows][heads][head_dim], dtype q_dtype (bf16, or fp32
  *        rounded to bf16 to nearest even on load), row stride q_row_stride elements.
  *   o  : device bf16 [round_q_rows][heads][head_dim], dense.
  *   lse: device fp32 [heads][round_q_rows] natural-log sum of exp of the scaled
  *        scores, or NULL.
+ *   workspace: NULL, or device memory of at least wave_attn_workspace() bytes
+ *        (current device), 256-byte aligned, owned by the caller, scratch
+ *        after the call: enables tail balancing.
  * scale multiplies Q.K (typically 1/sqrt(head_dim)).  Softmax in fp32, both
- * contractions in bf16 with fp32 accumulation.  Each node's result depends on
- * its query rows and the contents of its gather list only, with a fixed
- * reduction order, so it is bitwise the same in any schedule.  The plan's
- * q_tile must be WAVE_Q_TILE.  Asynchronous on `stream`. */
+ * contractions in bf16 with fp32 accumulation.  Without a workspace, each
+ * node's result depends on its query rows and the contents of its gather list
+ * only, with a fixed reduction order, so it is bitwise the same in any
+ * schedule; with one, the nodes of cut items differ from that by rounding
+ * (another reduction order).  The plan's q_tile must be WAVE_Q_TILE.
+ * Asynchronous on `stream`; calls that share a workspace must be ordered on
+ * one stream. */
 int32_t wave_attn(const wave_plan_t* plan, const void* d_desc, int32_t round,
                   const wave_kv_cache* cache, const void* q, int32_t q_dtype,
-                  int64_t q_row_stride, void* o, float* lse, float scale, void* stream);
+                  int64_t q_row_stride, void* o, float* lse, float scale,
+                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* Split-KV attention for short query chunks against long contexts (the
  * decode-shaped case: e.g. a chunk's 64 audio rows against tens of thousands

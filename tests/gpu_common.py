@@ -59,11 +59,13 @@ class HostInputs:
         return round_to_bf16(k).astype(np.float64), round_to_bf16(v).astype(np.float64)
 
 
-def gpu_rollout(plan, inputs, device, scale, src_dtype="fp32", poison=True, perturb=None, splits=None):
+def gpu_rollout(plan, inputs, device, scale, src_dtype="fp32", poison=True, perturb=None, splits=None,
+                balance=True):
     """Run every round of `plan` on the GPU; return {(chunk, level): (O fp32 [L,h,d], LSE [h,L])}.
 
     perturb(chunk, level, k, v) -> (k, v) may alter the fresh K/V of a slot.
     splits: None = wave_attn, else wave_attn_splitkv with that many splits (0 = auto).
+    balance: wave_attn's tail balancing (library's choice for this device).
     """
     import torch
     dt = torch.float32 if src_dtype == "fp32" else torch.bfloat16
@@ -85,7 +87,7 @@ def gpu_rollout(plan, inputs, device, scale, src_dtype="fp32", poison=True, pert
         nodes = plan.round_nodes(t).tolist()
         q = torch.from_numpy(np.concatenate([inputs.q(n[0], n[1]) for n in nodes])).to(device=device, dtype=dt)
         if splits is None:
-            o, lse = wv.wave_attn(plan, desc, t, cache, q, scale)
+            o, lse = wv.wave_attn(plan, desc, t, cache, q, scale, balance=balance)
         else:
             o, lse = wv.wave_attn_splitkv(plan, desc, t, cache, q, scale, num_splits=splits)
         torch.cuda.synchronize()

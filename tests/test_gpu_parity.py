@@ -11,7 +11,8 @@ import block_causal_attention_wave_amd as wv
 from oracle import plan as op
 from oracle.attention import round_to_bf16
 import wave_inputs as wi
-from gpu_common import (HostInputs, compare, gpu_rollout, log, oracle_rollout, sample_rows)
+from gpu_common import (HostInputs, LSE_ABS, MAX_ABS, MEAN_ABS, compare, gpu_rollout, log, oracle_rollout,
+                        sample_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -81,14 +82,17 @@ GRID = [
 ]
 
 
+@pytest.mark.parametrize("balance", [True, False])
 @pytest.mark.parametrize("policy,H,cond,L,heads,hd,dtype", GRID)
-def test_small_grid_parity(gpu_device, policy, H, cond, L, heads, hd, dtype):
+def test_small_grid_parity(gpu_device, policy, H, cond, L, heads, hd, dtype, balance):
+    """Every node of a B=5, K=3 rollout against the oracle, with and without tail
+    balancing (on 256 compute units these rounds cut all or some of their items)."""
     B, K = 5, 3
-    log(f"grid policy={policy} H={H} cond={cond} L={L} heads={heads} hd={hd} {dtype}")
+    log(f"grid policy={policy} H={H} cond={cond} L={L} heads={heads} hd={hd} {dtype} balance={balance}")
     plan = wv.wave_plan(B=B, K=K, policy=policy, sched=wv.WAVE, chunk_len=L, cond_len=cond, history_cap=H)
     inp = HostInputs(100 + L, heads, hd, L, cond, bf16=(dtype == "bf16"))
     scale = 1.0 / np.sqrt(hd)
-    got = gpu_rollout(plan, inp, gpu_device, scale, src_dtype=dtype)
+    got = gpu_rollout(plan, inp, gpu_device, scale, src_dtype=dtype, balance=balance)
     ref = oracle_rollout(B, K, policy, H, L, cond, inp, scale)
     assert set(got) == set(ref)
     for key in ref:
@@ -103,7 +107,7 @@ def test_serial_and_wave_schedules_bitwise_equal(gpu_device, policy):
     outs = {}
     for sched in (wv.SERIAL, wv.WAVE):
         plan = wv.wave_plan(B=B, K=K, policy=policy, sched=sched, chunk_len=L, cond_len=cond)
-        outs[sched] = gpu_rollout(plan, inp, gpu_device, 0.1, src_dtype="fp32")
+        outs[sched] = gpu_rollout(plan, inp, gpu_device, 0.1, src_dtype="fp32", balance=False)
     assert set(outs[wv.SERIAL]) == set(outs[wv.WAVE])
     for key in outs[wv.WAVE]:
         assert np.array_equal(outs[wv.SERIAL][key][0], outs[wv.WAVE][key][0]), key
@@ -333,3 +337,44 @@ def test_wide_score_range_parity(gpu_device, spread, hd, splits):
     for key in ref:
         s = compare(got[key][0], got[key][1], ref[key][0], ref[key][1], f"node {key}")
     log(f"  last node stats {s}")
+
+
+def test_tail_balancing_matches_unbalanced(gpu_device):
+    """The 832x480 seven-chunk K=4 round 6 at full size, with and without tail
+    balancing: rows of items processed whole are bitwise equal, rows of the cut
+    items agree to the parity bounds (another reduction order)."""
+    import torch
+    w = wi.WORKLOADS[2]
+    plan = wv.wave_plan(B=w.B, K=w.K, policy=wi.PROGRESSIVE, sched=wv.WAVE, chunk_len=w.chunk_len)
+    nbytes, items, splits = wv.attn_workspace(plan, w.round, w.heads, w.head_dim)
+    log(f"{w.name}: round {w.round}, tail balancing cuts {items} items x {splits}")
+    assert items > 0
+    desc = plan.upload(gpu_device)
+    cache = wv.KVCache(plan.num_phys_slots, w.heads, w.head_dim, plan.lpad(), gpu_device, fill=float("nan"))
+    for t in range(w.round + 1):
+        ws = plan.round_writes(t).tolist()
+        k_src = torch.cat([wi.device_tensor(w, 0, c, lv, "k", gpu_device, wi.PROGRESSIVE) for (c, lv, _, _) in ws])
+        v_src = torch.cat([wi.device_tensor(w, 0, c, lv, "v", gpu_device, wi.PROGRESSIVE) for (c, lv, _, _) in ws])
+        wv.kv_write(plan, desc, t, cache, k_src, v_src)
+    nodes = plan.round_nodes(w.round).tolist()
+    q = torch.cat([wi.device_tensor(w, 0, n[0], n[1], "q", gpu_device, wi.PROGRESSIVE) for n in nodes])
+    o0, l0 = wv.wave_attn(plan, desc, w.round, cache, q, w.scale, balance=False)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=gpu_device)
+    o1, l1 = wv.wave_attn(plan, desc, w.round, cache, q, w.scale, workspace=ws)
+    torch.cuda.synchronize()
+    o0, o1 = o0.float().cpu().numpy(), o1.float().cpu().numpy()
+    l0, l1 = l0.cpu().numpy(), l1.cpu().numpy()
+    assert np.isfinite(o1).all() and np.isfinite(l1).all()
+    b, e = int(plan.round_work_begin[w.round]), int(plan.round_work_begin[w.round + 1])
+    qoff = {i: int(n[4]) for i, n in enumerate(plan.nodes.tolist())}
+    cut = np.zeros(o0.shape[0], bool)
+    for node, q_start, q_rows, _ in plan.work[e - items:e].tolist():
+        r0 = qoff[node] + q_start
+        cut[r0:r0 + q_rows] = True
+    assert cut.any() and not cut.all()
+    assert np.array_equal(o0[~cut], o1[~cut]) and np.array_equal(l0[:, ~cut], l1[:, ~cut])
+    d = np.abs(o0[cut] - o1[cut])
+    log(f"  cut rows {int(cut.sum())}: max {d.max():.3g} mean {d.mean():.3g}, "
+        f"lse max {np.abs(l0[:, cut] - l1[:, cut]).max():.3g}")
+    assert d.max() <= MAX_ABS and d.mean() <= MEAN_ABS
+    assert np.abs(l0[:, cut] - l1[:, cut]).max() <= LSE_ABS

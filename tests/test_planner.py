@@ -169,7 +169,7 @@ def test_device_calls_validate_before_launch():
 
     def attn(round_=0, cache_=cache, q=fake, qd=0, stride=128, scale=0.125, desc=fake):
         return lib.wave_attn(pn.handle, desc, round_, C.byref(cache_), q, qd, stride, fake, None,
-                             scale, stream)
+                             scale, None, 0, stream)
 
     assert attn(round_=5) == _lib.WAVE_ERR_INVALID_ARG
     assert attn(round_=-1) == _lib.WAVE_ERR_INVALID_ARG
@@ -186,7 +186,7 @@ def test_device_calls_validate_before_launch():
     assert b"capacity" in lib.wave_last_error() or len(lib.wave_last_error()) > 0
     pn128 = native(4, 2, op.PROGRESSIVE, op.WAVE, -1, 128, 0, q_tile=128)
     assert lib.wave_attn(pn128.handle, fake, 0, C.byref(cache), fake, 0, 128, fake, None, 0.1,
-                         stream) == _lib.WAVE_ERR_UNSUPPORTED
+                         None, 0, stream) == _lib.WAVE_ERR_UNSUPPORTED
 
     # split-KV: workspace checks
     def split(ws=fake, nbytes=1 << 30, splits=2):
@@ -210,3 +210,46 @@ def test_device_calls_validate_before_launch():
     assert kvw(dt=5) == _lib.WAVE_ERR_UNSUPPORTED
     assert kvw(stride=10) == _lib.WAVE_ERR_INVALID_ARG
     assert kvw(src=C.c_void_p(0x10008)) == _lib.WAVE_ERR_UNSUPPORTED
+
+
+def test_tail_balancing_choice_and_workspace_checks():
+    """wave_attn's tail balancing: the memoised choice for the Wan2.1-1.3B round-6
+    shape (95 work items x 12 heads on 256 compute units) cuts some trailing
+    items; a single compute unit never pays for a cut; the workspace size
+    follows the documented layout; a misaligned or short workspace is rejected
+    on the host before any launch."""
+    lib = _lib.load()
+    w = WORKLOADS[2]
+    pn = native(w.B, w.K, op.PROGRESSIVE, op.WAVE, -1, w.chunk_len, 0)
+    b, m, s = C.c_size_t(), C.c_int32(), C.c_int32()
+    assert lib.wave_attn_workspace(pn.handle, w.round, w.heads, w.head_dim, 256, C.byref(b), C.byref(m),
+                                   C.byref(s)) == 0
+    items, splits = m.value, s.value
+    assert 1 <= items <= 95 and 2 <= splits <= 4
+    prows = items * 256
+    o_bytes = (splits * prows * w.heads * w.head_dim * 4 + 255) // 256 * 256
+    assert b.value == o_bytes + splits * w.heads * prows * 4
+    again = C.c_size_t()
+    assert lib.wave_attn_workspace(pn.handle, w.round, w.heads, w.head_dim, 256, C.byref(again), None,
+                                   None) == 0
+    assert again.value == b.value
+    assert lib.wave_attn_workspace(pn.handle, w.round, w.heads, w.head_dim, 1, C.byref(again), C.byref(m),
+                                   C.byref(s)) == 0
+    assert again.value == 0 and m.value == 0
+    for bad in ((w.round, 0, 128, 256), (w.round, 12, 96, 256), (w.round, 12, 128, -1), (99, 12, 128, 256)):
+        assert lib.wave_attn_workspace(pn.handle, *bad, C.byref(again), None, None) == _lib.WAVE_ERR_INVALID_ARG
+
+    # wave_attn itself (the device count falls back to 256 compute units without a GPU)
+    cache = _lib.KvCache(0x10000, 0x20000, pn.num_phys_slots, w.heads, w.head_dim, pn.lpad())
+    fake = C.c_void_p(0x10000)
+    dev_cus = C.c_size_t()
+    assert lib.wave_attn_workspace(pn.handle, w.round, w.heads, w.head_dim, 0, C.byref(dev_cus), None,
+                                   None) == 0
+
+    def attn(ws, nbytes):
+        return lib.wave_attn(pn.handle, fake, w.round, C.byref(cache), fake, 0, w.heads * w.head_dim, fake,
+                             None, 0.1, ws, nbytes, C.c_void_p(0))
+
+    if dev_cus.value > 0:
+        assert attn(C.c_void_p(0x10100), dev_cus.value - 1) == _lib.WAVE_ERR_CAPACITY
+    assert attn(C.c_void_p(0x10010), 1 << 40) == _lib.WAVE_ERR_INVALID_ARG
