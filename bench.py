@@ -281,6 +281,9 @@ def main():
             "algorithmic_tflop": round(flops / 1e12, 4),
         },
         "attn_ms": round(attn_avg, 4),
+        "attn_ms_median": round(float(np.median(attn_ms)), 4),
+        "attn_ms_p10": round(float(np.percentile(attn_ms, 10)), 4),
+        "attn_ms_p90": round(float(np.percentile(attn_ms, 90)), 4),
         "kv_write_ms": round(float(kvw_ms.mean()), 4),
         "round_ms": round(attn_avg + float(kvw_ms.mean()), 4),
         "pct_bf16_peak": round(100 * achieved / PEAK_BF16_TFLOPS, 2),
@@ -428,11 +431,18 @@ def cpu_baseline(w, plan, t_meas, nodes, policy, layer, device, rows_per_node):
     flops = algorithmic_flops(plan, t_meas, w.heads, w.head_dim, rows_per_node=len(rows))
     eprint(f"[bench] cpu oracle: {len(rows)} rows x {len(nodes)} nodes x {w.heads} heads in {secs:.1f} s "
            f"({threads} threads) = {flops / secs / 1e9:.2f} GFLOP/s")
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {
         "value": round(flops / secs / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
+        "cpu_model": cpu_model,
         "sample": f"{len(rows)} query rows of each of the {len(nodes)} nodes of round {t_meas}, "
                   f"all {w.heads} heads, fp64 dense-mask attention over every live slot; "
                   f"{secs:.1f} s wall; full-round estimate {secs * qlen / len(rows):.0f} s",
