@@ -18,6 +18,10 @@ Contents
 ``oracle.rollout``
     Serial rollout: executes a plan round by round against a dict cache keyed
     by logical slot, recomputing every node's context from phi.
+``oracle.chain``
+    The toy denoiser chain around the attention: seeded QKV projections with
+    a per-token RMS scale, K/V into the node's own slot, and each chunk's next
+    node consuming its previous node's last-layer attention output.
 
 Pins (values this oracle is checked against, other than itself) live in
 ``tests/test_oracle_*.py`` and ``tests/golden/``.  Every function here is

@@ -10,6 +10,10 @@ Recipe
   with which in {q, k, v}; the key is hashed with splitmix64 into a 63-bit
   seed.
 * Values are N(0, sigma^2) drawn in float32.
+* The toy denoiser chain adds, per layer, a projection matrix W [3D][D]
+  (D = heads * head_dim) drawn N(0, 1/D), keyed (workload seed, layer, "w"),
+  and per chunk a noise input X [L][D] drawn N(0, 1), keyed (workload seed,
+  chunk, "x").
 * The tiny workload draws on the host with numpy's PCG64 and hands float32 to
   the kernels (they round to bfloat16).  The large workloads draw on the
   device with a ``torch.Generator`` and round to bfloat16 with torch before
@@ -93,7 +97,7 @@ def _splitmix64(x: int) -> int:
 def tensor_seed(workload_key: int, layer: int, chunk: int, level: int, which: str,
                 policy: int = 0) -> int:
     """63-bit seed of one tensor; level COND_LEVEL marks a conditioning slot."""
-    w = {"q": 0, "k": 1, "v": 2}[which]
+    w = {"q": 0, "k": 1, "v": 2, "x": 3, "w": 4}[which]
     h = 0
     for part in (workload_key, policy, layer, chunk, level + 1, w):
         h = _splitmix64(h ^ (int(part) & _MASK64))
@@ -136,3 +140,37 @@ def device_tensor(w: Workload, layer, chunk, level, which, device, policy=0):
     shape = q_shape(w) if which == "q" else slot_shape(w, level)
     return device_normal_bf16(tensor_seed(w.key, layer, chunk, level, which, policy),
                               shape, w.sigma, device)
+
+
+# --- toy denoiser chain inputs ------------------------------------------------
+
+def chain_weight_seed(workload_key: int, layer: int) -> int:
+    """Seed of layer `layer`'s projection matrix."""
+    return tensor_seed(workload_key, layer, -1, -1, "w")
+
+
+def chain_noise_seed(workload_key: int, chunk: int) -> int:
+    """Seed of chunk `chunk`'s noise input (the input of its first update)."""
+    return tensor_seed(workload_key, 0, chunk, COND_LEVEL - 1, "x")
+
+
+def host_chain_weight(workload_key: int, layer: int, model_dim: int) -> np.ndarray:
+    """W [3D][D] float32, N(0, 1/D)."""
+    return host_normal(chain_weight_seed(workload_key, layer), (3 * model_dim, model_dim),
+                       float(1.0 / np.sqrt(model_dim)))
+
+
+def host_chain_noise(workload_key: int, chunk: int, tokens: int, model_dim: int) -> np.ndarray:
+    """X [L][D] float32, N(0, 1)."""
+    return host_normal(chain_noise_seed(workload_key, chunk), (tokens, model_dim), 1.0)
+
+
+def device_chain_weight(workload_key: int, layer: int, model_dim: int, device):
+    """W [3D][D] bfloat16 on the device, N(0, 1/D)."""
+    return device_normal_bf16(chain_weight_seed(workload_key, layer), (3 * model_dim, model_dim),
+                              float(1.0 / np.sqrt(model_dim)), device)
+
+
+def device_chain_noise(workload_key: int, chunk: int, tokens: int, model_dim: int, device):
+    """X [L][D] bfloat16 on the device, N(0, 1)."""
+    return device_normal_bf16(chain_noise_seed(workload_key, chunk), (tokens, model_dim), 1.0, device)
