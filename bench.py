@@ -124,6 +124,8 @@ def main():
                     help="wave_attn without tail balancing (each node bitwise independent of the schedule)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--rollout", action="store_true")
+    ap.add_argument("--chain", action="store_true",
+                    help="whole rollouts of the toy denoiser chain (QKV projection into the cache + attention)")
     ap.add_argument("--layers", type=int, default=0, help="rollout layers (0 = the workload's)")
     args = ap.parse_args()
 
@@ -137,6 +139,9 @@ def main():
     import wave_inputs as wi
 
     device = torch.device("cuda:0")
+    if args.chain:
+        chain_bench(args, device)
+        return
     if args.rollout:
         rollout_bench(args, device)
         return
@@ -311,6 +316,94 @@ def main():
     if copy_ms is not None:
         out["copy_1gib_ms"] = round(copy_ms, 4)
     print(json.dumps(out), flush=True)
+
+
+def chain_bench(args, device):
+    """Whole rollouts of the toy denoiser chain at the Wan2.1-1.3B shape: per
+    round and layer, qkv_project (K/V straight into the layer's cache, Q out)
+    then wave_attn; chain_store after the last layer.  Every node's input is
+    its chunk's previous output (seeded noise for the first update)."""
+    import torch
+    import block_causal_attention_wave_amd as wv
+    import wave_inputs as wi
+    key = args.workload if args.workload in (3, 4) else 3
+    w = wi.WORKLOADS[key]
+    layers = args.layers or w.layers
+    D = w.heads * w.head_dim
+    stream = torch.cuda.Stream()
+    results = []
+    for policy in ((wi.PROGRESSIVE,) if key == 3 else w.policies):
+        plan = wv.wave_plan(B=w.B, K=w.K, policy=policy, sched=wv.WAVE, chunk_len=w.chunk_len,
+                            history_cap=w.history_cap)
+        desc = plan.upload(device)
+        caches = [wv.KVCache(plan.num_phys_slots, w.heads, w.head_dim, plan.lpad(), device, fill=float("nan"))
+                  for _ in range(layers)]
+        weights = [wi.device_chain_weight(w.key, l, D, device) for l in range(layers)]
+        state = torch.stack([wi.device_chain_noise(w.key, c, w.chunk_len, D, device) for c in range(w.B)])
+        max_rows = int(plan.round_q_rows.max())
+        q = torch.empty((max_rows, w.heads, w.head_dim), dtype=torch.bfloat16, device=device)
+        o = [torch.empty((max_rows, w.heads, w.head_dim), dtype=torch.bfloat16, device=device) for _ in range(2)]
+        proj_ws = torch.empty(max_rows * 4 + 256, dtype=torch.uint8, device=device)
+        attn_bytes = max(wv.attn_workspace(plan, t, w.heads, w.head_dim)[0] for t in range(plan.num_rounds))
+        attn_ws = torch.empty(max(attn_bytes, 1), dtype=torch.uint8, device=device)
+        proj_ms = attn_ms = store_ms = 0.0
+        proj_flops = attn_flops = 0.0
+        round_ms = np.zeros(plan.num_rounds)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for t in range(plan.num_rounds):
+                rows = int(plan.round_q_rows[t])
+                attn_flops += algorithmic_flops(plan, t, w.heads, w.head_dim) * layers
+                proj_flops += 2.0 * rows * D * 3 * D * layers
+                x, layout = state, wv.X_CHUNK
+                for layer in range(layers):
+                    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                    ev[0].record(stream)
+                    wv.qkv_project(plan, desc, t, caches[layer], x, weights[layer], q=q[:rows], x_layout=layout,
+                                   workspace=proj_ws, stream=stream)
+                    ev[1].record(stream)
+                    ob = o[layer & 1][:rows]
+                    wv.wave_attn(plan, desc, t, caches[layer], q[:rows], w.scale, o=ob, want_lse=False,
+                                 stream=stream, workspace=attn_ws)
+                    ev[2].record(stream)
+                    ev[2].synchronize()
+                    proj_ms += ev[0].elapsed_time(ev[1])
+                    attn_ms += ev[1].elapsed_time(ev[2])
+                    round_ms[t] += ev[0].elapsed_time(ev[2])
+                    x, layout = ob.view(rows, D), wv.X_ROUND
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                wv.chain_store(plan, desc, t, o[(layers - 1) & 1][:rows], state, stream=stream)
+                e1.record(stream)
+                e1.synchronize()
+                store_ms += e0.elapsed_time(e1)
+                round_ms[t] += e0.elapsed_time(e1)
+        finite = bool(torch.isfinite(state.float()).all())
+        del caches, weights
+        torch.cuda.empty_cache()
+        total = float(round_ms.sum())
+        calls = plan.num_rounds * layers
+        res = {
+            "policy": wi.POLICY_NAMES[policy], "layers": layers, "rounds": plan.num_rounds,
+            "total_ms": round(total, 3), "ms_per_round": round(total / plan.num_rounds, 3),
+            "ms_per_chunk": round(total / w.B, 3),
+            "attention_tflops": round(attn_flops / (attn_ms * 1e-3) / 1e12, 1),
+            "projection_tflops": round(proj_flops / (proj_ms * 1e-3) / 1e12, 1),
+            "projection_ms_per_call": round(proj_ms / calls, 4),
+            "attention_ms_per_call": round(attn_ms / calls, 4),
+            "chain_store_ms_per_round": round(store_ms / plan.num_rounds, 4),
+            "projection_share": round(proj_ms / total, 4),
+            "finite": finite,
+        }
+        eprint(f"[chain] {w.name} {res['policy']}: {plan.num_rounds} rounds x {layers} layers, {total:.1f} ms "
+               f"total, {res['ms_per_round']:.2f} ms/round, {res['ms_per_chunk']:.2f} ms/chunk; attention "
+               f"{res['attention_tflops']:.0f} TFLOP/s, projection {res['projection_tflops']:.0f} TFLOP/s "
+               f"({res['projection_ms_per_call']:.3f} ms/call, {100 * res['projection_share']:.1f}% of the time)")
+        results.append(res)
+    print(json.dumps({"metric": "toy-chain rollout ms per round / per chunk; attention and projection TFLOP/s",
+                      "workload": w.name + "-toy-chain", "unit": "ms", "n_gpus": 1, "dtype": "bf16",
+                      "data": "synthetic", "timing": "sum of per-(round, layer) qkv_project + wave_attn and "
+                      "per-round chain_store event times", "results": results}), flush=True)
 
 
 def rollout_bench(args, device):

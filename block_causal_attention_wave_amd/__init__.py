@@ -245,3 +245,44 @@ def wave_attn_splitkv(plan: Plan, d_desc, round: int, cache: KVCache, q, scale: 
                                              float(scale), splits, C.c_void_p(workspace.data_ptr()),
                                              workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
     return o, lse
+
+
+# --- toy denoiser chain: the steps on either side of the attention ---------------
+
+X_ROUND, X_CHUNK = 0, 1
+
+
+def qkv_project_workspace_bytes(plan: Plan, round: int) -> int:
+    b = C.c_size_t()
+    _lib.check(_lib.load().qkv_project_workspace(plan.handle, round, C.byref(b)))
+    return b.value
+
+
+def qkv_project(plan: Plan, d_desc, round: int, cache: KVCache, x, w, q=None, x_layout=X_ROUND,
+                workspace=None, stream=None):
+    """QKV projection of every node of round `round` at one layer: K/V into the
+    nodes' own slots of `cache`, Q returned ([rows, heads, head_dim] bf16).
+
+    x: bf16 input rows, [round rows, D] (X_ROUND) or per-chunk state
+    [B, chunk_len, D] (X_CHUNK); w: bf16 [3D, D]."""
+    import torch
+    rows = int(plan.round_q_rows[round])
+    if q is None:
+        q = torch.empty((rows, cache.heads, cache.head_dim), dtype=torch.bfloat16, device=x.device)
+    nbytes = qkv_project_workspace_bytes(plan, round)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=x.device)
+    _lib.check(_lib.load().qkv_project(plan.handle, C.c_void_p(d_desc.data_ptr()), round, C.byref(cache.c),
+                                       C.c_void_p(x.data_ptr()), int(x_layout), C.c_void_p(w.data_ptr()),
+                                       C.c_void_p(q.data_ptr()), C.c_void_p(workspace.data_ptr()),
+                                       workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
+    return q
+
+
+def chain_store(plan: Plan, d_desc, round: int, o, state, stream=None):
+    """state[chunk of n] = o[rows of n] for every node n of round `round`
+    (o: [round rows, ..., ] bf16 with D values per row; state: [B, chunk_len, D])."""
+    model_dim = o[0].numel()
+    _lib.check(_lib.load().chain_store(plan.handle, C.c_void_p(d_desc.data_ptr()), round, model_dim,
+                                       C.c_void_p(o.data_ptr()), C.c_void_p(state.data_ptr()),
+                                       _stream_ptr(stream)))

@@ -24,7 +24,7 @@ WAVE_KEY_TILE = 64
 
 EXPORTS = ("wave_plan", "wave_plan_view_get", "wave_plan_desc_size", "wave_plan_desc_pack",
            "wave_plan_destroy", "kv_write", "wave_attn_workspace", "wave_attn", "wave_attn_splitkv_workspace",
-           "wave_attn_splitkv", "wave_last_error")
+           "wave_attn_splitkv", "qkv_project_workspace", "qkv_project", "chain_store", "wave_last_error")
 
 
 class PlanParams(C.Structure):
@@ -108,6 +108,13 @@ def load() -> C.CDLL:
                                       C.c_void_p, C.c_int32, C.c_int64, C.c_void_p, C.c_void_p,
                                       C.c_float, C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p]
     lib.wave_attn_splitkv.restype = C.c_int32
+    lib.qkv_project_workspace.argtypes = [C.c_void_p, C.c_int32, C.POINTER(C.c_size_t)]
+    lib.qkv_project_workspace.restype = C.c_int32
+    lib.qkv_project.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.POINTER(KvCache), C.c_void_p, C.c_int32,
+                                C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+    lib.qkv_project.restype = C.c_int32
+    lib.chain_store.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]
+    lib.chain_store.restype = C.c_int32
     lib.wave_last_error.argtypes = []
     lib.wave_last_error.restype = C.c_char_p
     _lib = lib

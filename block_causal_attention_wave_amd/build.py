@@ -30,10 +30,12 @@ SOURCES = [
     ("abi.cpp", False),
     ("kv_write.hip", True),
     ("wave_attn.hip", True),
+    ("qkv_proj.hip", True),
 ]
-# Per-source extra flags.  wave_attn sets M0 in inline asm for its direct
-# global->LDS loads; clang warns about clobbering that reserved register.
-EXTRA = {"wave_attn.hip": ["-Wno-inline-asm"]}
+# Per-source extra flags.  The attention and projection kernels set M0 in
+# inline asm for their direct global->LDS loads; clang warns about clobbering
+# that reserved register.
+EXTRA = {"wave_attn.hip": ["-Wno-inline-asm"], "qkv_proj.hip": ["-Wno-inline-asm"]}
 
 
 def _compile(src: str, device: bool) -> str:

@@ -16,6 +16,8 @@
 #include "planner.hpp"
 #include "wave.h"
 
+static_assert(wave::kNodeStride == wave::kDescNodeWords, "descriptor node rows: planner and kernels disagree");
+
 struct wave_plan {
   wave::Plan p;
   // tail-balancing choices, memoised per (round, heads, head_dim, compute units)
@@ -362,6 +364,105 @@ int32_t wave_attn_splitkv(const wave_plan_t* plan, const void* d_desc, int32_t r
   }
   const hipError_t e = wave::launch_wave_attn(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return set_error(WAVE_ERR_HIP, std::string("wave_attn_splitkv: ") + hipGetErrorString(e));
+  return ok();
+}
+
+namespace {
+
+int32_t chain_plan_check(const wave::Plan& p, const std::string& f) {
+  if (p.params.cond_len != 0 || (p.params.query_len != 0 && p.params.query_len != p.params.chunk_len))
+    return set_error(WAVE_ERR_UNSUPPORTED, f + ": the chain needs cond_len = 0 and query rows = chunk tokens");
+  return WAVE_OK;
+}
+
+}  // namespace
+
+int32_t qkv_project_workspace(const wave_plan_t* plan, int32_t round, size_t* bytes) {
+  if (!plan || !bytes) return set_error(WAVE_ERR_INVALID_ARG, "qkv_project_workspace: null argument");
+  const wave::Plan& p = plan->p;
+  if (round < 0 || round >= p.num_rounds())
+    return set_error(WAVE_ERR_INVALID_ARG, "qkv_project_workspace: round out of range");
+  *bytes = static_cast<size_t>(p.round_q_rows[round]) * sizeof(float);
+  return ok();
+}
+
+int32_t qkv_project(const wave_plan_t* plan, const void* d_desc, int32_t round, const wave_kv_cache* cache,
+                    const void* x, int32_t x_layout, const void* w, void* q, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  const std::string f("qkv_project");
+  int32_t rc = check_common(plan, d_desc, round, cache, "qkv_project");
+  if (rc != WAVE_OK) return rc;
+  const wave::Plan& p = plan->p;
+  rc = chain_plan_check(p, f);
+  if (rc != WAVE_OK) return rc;
+  if (!x || !w || !q) return set_error(WAVE_ERR_INVALID_ARG, f + ": null x, w or q");
+  if (x_layout != WAVE_X_ROUND && x_layout != WAVE_X_CHUNK)
+    return set_error(WAVE_ERR_INVALID_ARG, f + ": x_layout must be WAVE_X_ROUND or WAVE_X_CHUNK");
+  if (!aligned16(x) || !aligned16(w) || !aligned16(q))
+    return set_error(WAVE_ERR_UNSUPPORTED, f + ": x, w and q must be 16-byte aligned");
+  const int64_t D = static_cast<int64_t>(cache->heads) * cache->head_dim;
+  if (D % 128 != 0) return set_error(WAVE_ERR_UNSUPPORTED, f + ": heads * head_dim must be a multiple of 128");
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+    return set_error(WAVE_ERR_INVALID_ARG, f + ": workspace must be non-null and 256-byte aligned");
+  if (workspace_bytes < static_cast<size_t>(p.round_q_rows[round]) * sizeof(float))
+    return set_error(WAVE_ERR_CAPACITY, f + ": workspace smaller than qkv_project_workspace()");
+  const int32_t n0 = p.round_node_begin[round], n1 = p.round_node_begin[round + 1];
+  const int32_t row_tiles = (cache->lpad + 127) / 128;
+  const int32_t col_tiles = static_cast<int32_t>(3 * D / 128);
+  if (static_cast<int64_t>(n1 - n0) * row_tiles * col_tiles > INT32_MAX ||
+      static_cast<int64_t>(p.params.chunk_len) * D * 2 > UINT32_MAX)
+    return set_error(WAVE_ERR_UNSUPPORTED, f + ": too many workgroups or chunk rows too large");
+  const int32_t* desc = static_cast<const int32_t*>(d_desc);
+  wave::ProjArgs a{};
+  a.nodes = desc + p.desc[8];
+  a.ctx = desc + p.desc[9];
+  a.node_begin = n0;
+  a.num_nodes = n1 - n0;
+  a.max_rows = p.params.chunk_len;
+  a.row_tiles = row_tiles;
+  a.col_tiles = col_tiles;
+  a.x = x;
+  a.x_chunk = x_layout == WAVE_X_CHUNK;
+  a.chunk_rows = p.params.chunk_len;
+  a.w = w;
+  a.model_dim = static_cast<int32_t>(D);
+  a.heads = cache->heads;
+  a.head_dim = cache->head_dim;
+  a.lpad = cache->lpad;
+  a.k = cache->k;
+  a.vt = cache->vt;
+  a.q = q;
+  a.row_scale = static_cast<float*>(workspace);
+  const hipError_t e = wave::launch_qkv_project(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return set_error(WAVE_ERR_HIP, f + ": " + hipGetErrorString(e));
+  return ok();
+}
+
+int32_t chain_store(const wave_plan_t* plan, const void* d_desc, int32_t round, int32_t model_dim,
+                    const void* o, void* state, void* stream) {
+  const std::string f("chain_store");
+  if (!plan || !d_desc || !o || !state) return set_error(WAVE_ERR_INVALID_ARG, f + ": null argument");
+  const wave::Plan& p = plan->p;
+  if (round < 0 || round >= p.num_rounds()) return set_error(WAVE_ERR_INVALID_ARG, f + ": round out of range");
+  const int32_t rc = chain_plan_check(p, f);
+  if (rc != WAVE_OK) return rc;
+  if (model_dim < 8 || model_dim % 8 != 0)
+    return set_error(WAVE_ERR_INVALID_ARG, f + ": model_dim must be a positive multiple of 8");
+  if (!aligned16(o) || !aligned16(state) || !aligned16(d_desc))
+    return set_error(WAVE_ERR_UNSUPPORTED, f + ": o, state and the descriptor must be 16-byte aligned");
+  const int64_t n16 = static_cast<int64_t>(p.params.chunk_len) * model_dim / 8;
+  if ((n16 + 255) / 256 > INT32_MAX) return set_error(WAVE_ERR_UNSUPPORTED, f + ": chunk too large");
+  wave::StoreArgs a{};
+  a.nodes = static_cast<const int32_t*>(d_desc) + p.desc[8];
+  a.node_begin = p.round_node_begin[round];
+  a.num_nodes = p.round_node_begin[round + 1] - a.node_begin;
+  a.max_rows = p.params.chunk_len;
+  a.model_dim = model_dim;
+  a.chunk_rows = p.params.chunk_len;
+  a.o = o;
+  a.state = state;
+  const hipError_t e = wave::launch_chain_store(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return set_error(WAVE_ERR_HIP, f + ": " + hipGetErrorString(e));
   return ok();
 }
 

@@ -7,6 +7,11 @@
 
 namespace wave {
 
+// Words per node row of the device descriptor: q_offset, q_len, ctx_begin,
+// ctx_count, chunk, level.  A node's own slot is the last entry of its
+// gather list.
+constexpr int kDescNodeWords = 6;
+
 // One round's K/V write.  `writes` points at the round's rows of the write
 // table in the device descriptor (phys_slot, len, src_offset, 0 per row).
 struct KvWriteArgs {
@@ -54,7 +59,36 @@ struct AttnArgs {
   float* part_lse;
 };
 
+// Toy-chain QKV projection of one round at one layer: every node's input
+// rows x (round-packed [round rows][D], or per-chunk state [chunks][chunk_rows][D]
+// when x_chunk) times W^T ([3D][D]), scaled per row by 1/rms (row_scale,
+// indexed by round row), to Q (round-packed [rows][D]) and the node's own
+// K / V^T cache slot.  Workgroups: (node, row tile, column tile).
+struct ProjArgs {
+  const int32_t* nodes;
+  const int32_t* ctx;
+  int32_t node_begin, num_nodes, max_rows, row_tiles, col_tiles;
+  const void* x;
+  int32_t x_chunk, chunk_rows;
+  const void* w;
+  int32_t model_dim, heads, head_dim, lpad;
+  void* k;
+  void* vt;
+  void* q;
+  float* row_scale;
+};
+
+// Copy of each node's output rows o[q_offset ..] to its chunk's state rows.
+struct StoreArgs {
+  const int32_t* nodes;
+  int32_t node_begin, num_nodes, max_rows, model_dim, chunk_rows;
+  const void* o;
+  void* state;
+};
+
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
+hipError_t launch_qkv_project(const ProjArgs& a, hipStream_t stream);
+hipError_t launch_chain_store(const StoreArgs& a, hipStream_t stream);
 hipError_t launch_wave_attn(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace wave

@@ -335,6 +335,8 @@ int32_t build_plan(const wave_plan_params& pin, Plan& out, std::string* err) {
     r[1] = pl.nodes[k].q_len;
     r[2] = pl.nodes[k].ctx_begin;
     r[3] = pl.nodes[k].ctx_count;
+    r[4] = pl.nodes[k].chunk;
+    r[5] = pl.nodes[k].level;
   }
   for (int32_t k = 0; k < nc; ++k) {
     int32_t* r = d + off_ctx + static_cast<int64_t>(k) * kCtxStride;

@@ -16,13 +16,13 @@ namespace wave {
 //   [7..11] word offsets of the round, node, ctx, write and work tables.
 // Tables (one row per element, fixed stride):
 //   round : node_begin, node_end, write_begin, write_end, work_begin, work_end, q_rows, src_rows
-//   node  : q_offset, q_len, ctx_begin, ctx_count
+//   node  : q_offset, q_len, ctx_begin, ctx_count, chunk, level
 //   ctx   : phys_slot, len
 //   write : phys_slot, len, src_offset, 0
 //   work  : node, q_start, q_rows, 0
 constexpr int32_t kDescMagic = 0x57415645;  // "WAVE"
-constexpr int32_t kDescVersion = 1;
-constexpr int kRoundStride = 8, kNodeStride = 4, kCtxStride = 2, kWriteStride = 4, kWorkStride = 4;
+constexpr int32_t kDescVersion = 2;
+constexpr int kRoundStride = 8, kNodeStride = 6, kCtxStride = 2, kWriteStride = 4, kWorkStride = 4;
 constexpr int kDescHeader = 12;
 
 struct Plan {

@@ -1,0 +1,256 @@
+// qkv_project and chain_store: the steps on either side of the attention in
+// the toy denoiser chain, on gfx950.
+//
+// The pages carry no model, so a seeded stand-in closes the loop between
+// denoising levels: a chunk's next node consumes its previous node's output
+// (Wave Forcing summary, mechanism paragraph; design-space paper, Figure 2),
+// and every node projects its input to Q, K and V.  Per layer:
+//   [Q | K | V] = bf16( (A W^T) / rms(A) ),  rms(a) = sqrt(mean_c a_c^2 + 1e-6)
+// with A the node's input rows [L][D] (D = heads * head_dim) and W [3D][D].
+// The K and V columns go straight into the node's own cache slot (K
+// token-major, V transposed, zero past the chunk's tokens), so no separate
+// K/V copy pass is needed; Q goes to the round's packed query rows.
+//
+// Kernels:
+//   row_scale_kernel  1 / rms of every input row (one wave per row).
+//   qkv_gemm_kernel   one workgroup per (node, 128-token tile, 128-column
+//                     tile): bf16 MFMA 32x32x16, fp32 accumulation, a
+//                     two-stage LDS ring of 128x64 A and W tiles filled by
+//                     direct global->LDS loads, and an epilogue that scales,
+//                     rounds and scatters the tile through LDS.
+//   chain_store_kernel  copies each node's output rows to its chunk's state.
+#include <hip/hip_runtime.h>
+
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace wave {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int TM = 128, TN = 128, TK = 64;
+constexpr int THREADS = 256;
+constexpr int ROW_BYTES = TK * 2;            // one tile row in LDS
+constexpr int TILE_BYTES = TM * ROW_BYTES;   // 16 KiB (A and W tiles alike)
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // A tile then W tile
+constexpr int LOADS = TILE_BYTES / (THREADS * 16);  // 16-byte loads per thread per tile
+constexpr int OUT_PITCH = (TN + 8) * 2;      // bytes per row of the staged output tile
+static_assert(TM == TN, "A and W tiles share one layout");
+static_assert(TM * OUT_PITCH <= 2 * STAGE_BYTES, "the output tile fits in the ring");
+
+// 16-byte chunk swizzle of a 128-byte LDS row: a 16-byte LDS read is served
+// 16 lanes at a time (a half-wave's lane quads of equal index parity), and an
+// MFMA operand read puts consecutive lanes on consecutive rows at one chunk.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+// 1 / rms of each input row of the round's nodes: grid (row blocks, nodes),
+// one wave per row.
+__global__ __launch_bounds__(256) void row_scale_kernel(ProjArgs a) {
+  const int node = a.node_begin + blockIdx.y;
+  const int32_t* nd = a.nodes + kDescNodeWords * node;
+  const int q_offset = nd[0], L = nd[1], chunk = nd[4];
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (r >= L) return;
+  const int64_t src_row = (a.x_chunk ? (int64_t)chunk * a.chunk_rows : (int64_t)q_offset) + r;
+  const bf16x8* row = reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.x) + src_row * a.model_dim);
+  float ss = 0.0f;
+  for (int c = lane; c < a.model_dim / 8; c += 64) {
+    const bf16x8 v = row[c];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss = __builtin_fmaf((float)v[i], (float)v[i], ss);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+  if (lane == 0) a.row_scale[q_offset + r] = 1.0f / __builtin_sqrtf(ss / (float)a.model_dim + 1e-6f);
+}
+
+template <int HD>
+__global__ __launch_bounds__(THREADS, 2) void qkv_gemm_kernel(ProjArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wv >> 1, wc = wv & 1;  // this wave's 64x64 quarter of the tile
+  int b = blockIdx.x;
+  const int ct = b % a.col_tiles;
+  b /= a.col_tiles;
+  const int rt = b % a.row_tiles;
+  const int node = a.node_begin + b / a.row_tiles;
+  const int32_t* nd = a.nodes + kDescNodeWords * node;
+  const int q_offset = nd[0], L = nd[1], chunk = nd[4];
+  const int phys = a.ctx[2 * (nd[2] + nd[3] - 1)];  // the node's own slot: last in its gather list
+  const int D = a.model_dim;
+  const int r0 = rt * TM, c0 = ct * TN;
+
+  // Per-lane byte offsets of this thread's tile loads (A rows past the
+  // chunk's tokens re-read its last row; their results are dropped).
+  const char* abase = static_cast<const char*>(a.x) +
+                      ((a.x_chunk ? (int64_t)chunk * a.chunk_rows : (int64_t)q_offset) * D) * 2;
+  const char* wbase = static_cast<const char*>(a.w) + (int64_t)c0 * D * 2;
+  uint32_t aoff[LOADS], woff[LOADS];
+#pragma unroll
+  for (int n = 0; n < LOADS; ++n) {
+    const int off = (wv * LOADS + n) * 1024 + lane * 16;
+    const int row = off / ROW_BYTES;
+    const int lc = ((off % ROW_BYTES) / 16) ^ swz(row);
+    aoff[n] = (uint32_t)(((int64_t)min(r0 + row, L - 1) * D + lc * 8) * 2);
+    woff[n] = (uint32_t)(((int64_t)row * D + lc * 8) * 2);
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+  auto issue = [&](int ks, int stage) {
+    const char* ab = abase + (int64_t)ks * TK * 2;
+    const char* wb = wbase + (int64_t)ks * TK * 2;
+    const uint32_t sa = lds0 + stage * STAGE_BYTES, sw = sa + TILE_BYTES;
+#pragma unroll
+    for (int n = 0; n < LOADS; ++n) load_lds16(sa + (wv * LOADS + n) * 1024, ab, aoff[n]);
+#pragma unroll
+    for (int n = 0; n < LOADS; ++n) load_lds16(sw + (wv * LOADS + n) * 1024, wb, woff[n]);
+  };
+  auto barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  constexpr int kWaitExp = (0x7 << 4) | (0xF << 8);  // wait on vmcnt only
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const int nk = D / TK;
+  issue(0, 0);
+  for (int ks = 0; ks < nk; ++ks) {
+    if (ks + 1 < nk) {
+      issue(ks + 1, (ks + 1) & 1);
+      __builtin_amdgcn_s_waitcnt(kWaitExp | (2 * LOADS));  // this step's tiles have landed
+    } else {
+      __builtin_amdgcn_s_waitcnt(kWaitExp);
+    }
+    barrier();
+    const char* sa = lds + (ks & 1) * STAGE_BYTES;
+    const char* sw = sa + TILE_BYTES;
+#pragma unroll
+    for (int s = 0; s < TK / 16; ++s) {
+      bf16x8 af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = wr * 64 + i * 32 + (lane & 31);
+        af[i] = *reinterpret_cast<const bf16x8*>(sa + row * ROW_BYTES + (((2 * s + (lane >> 5)) ^ swz(row)) * 16));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = wc * 64 + j * 32 + (lane & 31);
+        bf[j] = *reinterpret_cast<const bf16x8*>(sw + row * ROW_BYTES + (((2 * s + (lane >> 5)) ^ swz(row)) * 16));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    barrier();  // the next issue overwrites this stage
+  }
+
+  // Epilogue: scale rows by 1/rms (0 past the chunk's tokens), round to bf16
+  // and stage the tile in LDS: row-major for Q and K columns, column-major
+  // (tokens contiguous) for V columns.
+  const int part = c0 / D;  // 0: Q, 1: K, 2: V (D is a multiple of TN)
+  // MFMA 32x32 accumulator: register e of lane l is row 8(e/4) + 4(l/32) + e%4, column l%32.
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int row0 = wr * 64 + i * 32 + 8 * g + 4 * (lane >> 5);
+      float sc[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = r0 + row0 + e;
+        sc[e] = r < L ? a.row_scale[q_offset + r] : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = wc * 64 + j * 32 + (lane & 31);
+        if (part == 2) {
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[i][j][4 * g + e] * sc[e]);
+          *reinterpret_cast<bf16x4*>(lds + col * OUT_PITCH + row0 * 2) = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            *reinterpret_cast<__bf16*>(lds + (row0 + e) * OUT_PITCH + col * 2) = (__bf16)(acc[i][j][4 * g + e] * sc[e]);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int heads = a.heads, lpad = a.lpad;
+  for (int id = tid; id < TM * (TN / 8); id += THREADS) {
+    if (part == 2) {
+      const int col = id / (TM / 8), tok = r0 + (id % (TM / 8)) * 8;
+      if (tok >= lpad) continue;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + col * OUT_PITCH + (tok - r0) * 2);
+      const int h = (c0 - 2 * D + col) / HD, dd = (c0 - 2 * D + col) % HD;
+      __bf16* dst = static_cast<__bf16*>(a.vt) + (((int64_t)phys * heads + h) * HD + dd) * lpad + tok;
+      *reinterpret_cast<u32x4*>(dst) = v;
+    } else {
+      const int row = id / (TN / 8), cc = (id % (TN / 8)) * 8;
+      const int r = r0 + row;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * OUT_PITCH + cc * 2);
+      if (part == 0) {
+        if (r >= L) continue;
+        __bf16* dst = static_cast<__bf16*>(a.q) + (int64_t)(q_offset + r) * D + c0 + cc;
+        *reinterpret_cast<u32x4*>(dst) = v;
+      } else {
+        if (r >= lpad) continue;
+        const int h = (c0 - D + cc) / HD, dd = (c0 - D + cc) % HD;
+        __bf16* dst = static_cast<__bf16*>(a.k) + (((int64_t)phys * heads + h) * lpad + r) * HD + dd;
+        *reinterpret_cast<u32x4*>(dst) = v;
+      }
+    }
+  }
+}
+
+// state[chunk rows] = o[node rows] for every node of the round: grid (row
+// chunks of 256 x 8 elements, nodes).
+__global__ __launch_bounds__(256) void chain_store_kernel(StoreArgs a) {
+  const int node = a.node_begin + blockIdx.y;
+  const int32_t* nd = a.nodes + kDescNodeWords * node;
+  const int q_offset = nd[0], L = nd[1], chunk = nd[4];
+  const int64_t n16 = (int64_t)L * a.model_dim / 8;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n16) return;
+  const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(a.o) + (int64_t)q_offset * a.model_dim);
+  u32x4* dst = reinterpret_cast<u32x4*>(static_cast<__bf16*>(a.state) + (int64_t)chunk * a.chunk_rows * a.model_dim);
+  dst[i] = src[i];
+}
+
+}  // namespace
+
+hipError_t launch_qkv_project(const ProjArgs& a, hipStream_t stream) {
+  if (a.num_nodes == 0) return hipSuccess;
+  dim3 sgrid((unsigned)((a.max_rows + 3) / 4), (unsigned)a.num_nodes);
+  hipLaunchKernelGGL(row_scale_kernel, sgrid, dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 grid((unsigned)(a.num_nodes * a.row_tiles * a.col_tiles));
+  if (a.head_dim == 128) hipLaunchKernelGGL(qkv_gemm_kernel<128>, grid, dim3(THREADS), 0, stream, a);
+  else hipLaunchKernelGGL(qkv_gemm_kernel<64>, grid, dim3(THREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_chain_store(const StoreArgs& a, hipStream_t stream) {
+  if (a.num_nodes == 0) return hipSuccess;
+  const int64_t n16 = (int64_t)a.max_rows * a.model_dim / 8;
+  dim3 grid((unsigned)((n16 + 255) / 256), (unsigned)a.num_nodes);
+  hipLaunchKernelGGL(chain_store_kernel, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace wave

@@ -35,6 +35,7 @@
 
 #include <type_traits>
 
+#include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace wave {
@@ -115,20 +116,6 @@ struct TileOffsets {
     }
   }
 };
-
-// One 16-byte-per-lane direct global->LDS load: lane i's 16 bytes at
-// base + off land at LDS address lds_addr + 16*i.  Written as inline asm so
-// that the compiler does not treat the asynchronous LDS write as aliasing the
-// ring stages being read (it would then wait for every in-flight tile before
-// each LDS read); completion is tracked explicitly with s_waitcnt vmcnt and
-// the tile barrier.  The instruction has no register results.  M0 is set here
-// and used by nothing else in this kernel.
-__device__ __forceinline__ void load_lds16(uint32_t lds_addr, const char* base, uint32_t off) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(lds_addr), "v"(off), "s"(base)
-               : "memory", "m0");
-}
 
 // Issue one thread's direct global->LDS loads of a 64-key K tile (rows
 // permuted, chunks swizzled) and the matching V^T tile.  kt / vt point at the
@@ -386,7 +373,7 @@ void wave_attn_kernel(AttnArgs a) {
   }
   const int32_t* wk = a.work + 4 * (a.work_begin + item);
   const int node = wk[0], q_start = wk[1], q_rows = wk[2];
-  const int32_t* nd = a.nodes + 4 * node;
+  const int32_t* nd = a.nodes + kDescNodeWords * node;
   const int q_offset = nd[0], ctx_count = nd[3];
   const int32_t* ctx_g = a.ctx + 2 * nd[2];
   // first partial row of this item (split-KV: its round row)
@@ -685,7 +672,7 @@ __global__ __launch_bounds__(256) void wave_attn_combine_kernel(AttnArgs a) {
     const int32_t* wk = a.work + 4 * (a.work_begin + a.num_direct + (int)(prow / kQTile));
     const int r = (int)(prow % kQTile);
     if (r >= wk[2]) return;
-    row = (int64_t)a.nodes[4 * wk[0]] + wk[1] + r;
+    row = (int64_t)a.nodes[kDescNodeWords * wk[0]] + wk[1] + r;
     S = a.tail_splits;
   }
   const int64_t rows = a.lse_stride;

@@ -233,6 +233,46 @@ int32_t wave_attn_splitkv(const wave_plan_t* plan, const void* d_desc, int32_t r
                           int32_t num_splits, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* ---- Toy denoiser chain: the steps on either side of the attention ----
+ *
+ * The pages carry no model weights; a seeded stand-in closes the loop between
+ * denoising levels so that a chunk's next node consumes its previous node's
+ * result (Wave Forcing summary, mechanism paragraph; design-space paper,
+ * Figure 2: a chunk advances one denoising step per round, and the refresh
+ * pass consumes the finished chunk).  Per layer of a node:
+ *   [Q | K | V] = bf16( (A W^T) / rms(A) ),  rms(a) = sqrt(mean_c a_c^2 + 1e-6)
+ * A: the node's input rows [chunk_len][D], D = heads * head_dim; W [3D][D].
+ * The chain needs plans with cond_len = 0 and query rows = chunk tokens. */
+
+/* x_layout of qkv_project */
+#define WAVE_X_ROUND 0 /* x is [round_q_rows][D], packed like the round's Q (e.g. the previous layer's O) */
+#define WAVE_X_CHUNK 1 /* x is per-chunk state [B][chunk_len][D] (chain_store's layout) */
+
+/* Workspace of qkv_project for round `round`: one fp32 per query row. */
+int32_t qkv_project_workspace(const wave_plan_t* plan, int32_t round, size_t* bytes);
+
+/* QKV projection of every node of round `round` at one layer.
+ *   cache: the layer's cache; each node's K and V^T go into its own slot (the
+ *          last entry of its gather list), tokens [chunk_len, lpad) zeroed.
+ *          Replaces kv_write for chain rounds.
+ *   x    : device bf16 input rows, layout x_layout.
+ *   w    : device bf16 [3D][D]; row o holds output column o's weights
+ *          (o < D: Q, then K, then V; column = head * head_dim + dim).
+ *   q    : device bf16 [round_q_rows][heads][head_dim] (wave_attn's q).
+ *   workspace: >= qkv_project_workspace() bytes, 256-byte aligned.
+ * D must be a multiple of 128.  Asynchronous on `stream`. */
+int32_t qkv_project(const wave_plan_t* plan, const void* d_desc, int32_t round,
+                    const wave_kv_cache* cache, const void* x, int32_t x_layout,
+                    const void* w, void* q, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* state[chunk(n)] = o[rows of n] for every node n of round `round`:
+ *   o    : device bf16 [round_q_rows][model_dim] (wave_attn's o of the last layer).
+ *   state: device bf16 [B][chunk_len][model_dim].
+ * model_dim a positive multiple of 8.  Asynchronous on `stream`. */
+int32_t chain_store(const wave_plan_t* plan, const void* d_desc, int32_t round, int32_t model_dim,
+                    const void* o, void* state, void* stream);
+
 /* Message of the last failed call on this thread ("" if none).  Valid until
  * the next call into this library from the same thread. */
 const char* wave_last_error(void);

@@ -1,0 +1,193 @@
+"""GPU tests of the toy denoiser chain: qkv_project, chain_store and whole chains.
+
+Expected values come from ``oracle.chain`` only; inputs from ``wave_inputs``.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import block_causal_attention_wave_amd as wv
+from oracle import chain as oc
+from oracle import plan as op
+from oracle.attention import round_to_bf16
+import wave_inputs as wi
+from gpu_common import log
+
+pytestmark = pytest.mark.gpu
+
+
+def bf16(x):
+    return round_to_bf16(np.asarray(x, np.float32))
+
+
+def _inputs(key, B, L, heads, hd, layers):
+    D = heads * hd
+    noise = {c: bf16(wi.host_chain_noise(key, c, L, D)) for c in range(B)}
+    weights = [bf16(wi.host_chain_weight(key, l, D)) for l in range(layers)]
+    return noise, weights
+
+
+def gpu_chain(plan, B, L, heads, hd, noise, weights, scale, device, balance=False):
+    """Run the chain over `plan` on the GPU; return {(chunk, level): [O per layer as [L, heads, hd] fp32]}."""
+    import torch
+    D = heads * hd
+    layers = len(weights)
+    desc = plan.upload(device)
+    caches = [wv.KVCache(plan.num_phys_slots, heads, hd, plan.lpad(), device, fill=float("nan"))
+              for _ in range(layers)]
+    w_dev = [torch.from_numpy(w).to(device=device, dtype=torch.bfloat16) for w in weights]
+    state = torch.from_numpy(np.stack([noise[c] for c in range(B)])).to(device=device, dtype=torch.bfloat16)
+    outs = {}
+    for t in range(plan.num_rounds):
+        rows = int(plan.round_q_rows[t])
+        x, layout = state, wv.X_CHUNK
+        per_layer = []
+        for layer in range(layers):
+            q = wv.qkv_project(plan, desc, t, caches[layer], x, w_dev[layer], x_layout=layout)
+            o, _ = wv.wave_attn(plan, desc, t, caches[layer], q, scale, balance=balance)
+            per_layer.append(o)
+            x, layout = o.view(rows, D), wv.X_ROUND
+        wv.chain_store(plan, desc, t, per_layer[-1], state)
+        torch.cuda.synchronize()
+        for n in plan.round_nodes(t).tolist():
+            a, b = n[4], n[4] + n[5]
+            outs[(n[0], n[1])] = [o[a:b].float().cpu().numpy() for o in per_layer]
+    return outs
+
+
+@pytest.mark.parametrize("heads,hd,L,layout", [(2, 64, 300, wv.X_CHUNK), (1, 128, 129, wv.X_ROUND),
+                                               (3, 128, 200, wv.X_CHUNK), (4, 64, 64, wv.X_ROUND)])
+def test_qkv_project_parity(gpu_device, heads, hd, L, layout):
+    """Q, K and V^T of one round against oracle.chain.project on the same bf16
+    inputs, slot tails exactly zero, slots of other rounds untouched.  Bound
+    per element: one bf16 rounding step (2^-7 relative) on top of the fp32
+    summation error of a D-term dot product, gamma * sum_c |a_c w_oc| / rms(a)
+    with gamma = D * 2^-24 (the standard worst-case bound for recursive
+    summation); the latter matters only where the sum cancels to near zero."""
+    import torch
+    D = heads * hd
+    plan = wv.wave_plan(B=3, K=2, policy=wi.PROGRESSIVE, sched=wv.WAVE, chunk_len=L)
+    t = 2  # three nodes: U(0,...), U(1,...) and one more
+    nodes = plan.round_nodes(t).tolist()
+    rows = int(plan.round_q_rows[t])
+    log(f"qkv_project heads={heads} hd={hd} L={L} layout={layout} nodes={[(n[0], n[1]) for n in nodes]}")
+    rng = np.random.default_rng(11)
+    w = bf16(rng.standard_normal((3 * D, D)) / math.sqrt(D))
+    if layout == wv.X_CHUNK:
+        x_host = bf16(rng.standard_normal((3, L, D)) * 1.5)
+        a_of = {(n[0], n[1]): x_host[n[0]] for n in nodes}
+    else:
+        x_host = bf16(rng.standard_normal((rows, D)) * 0.7)
+        a_of = {(n[0], n[1]): x_host[n[4]:n[4] + n[5]] for n in nodes}
+    desc = plan.upload(gpu_device)
+    cache = wv.KVCache(plan.num_phys_slots, heads, hd, plan.lpad(), gpu_device, fill=float("nan"))
+    x = torch.from_numpy(x_host).to(device=gpu_device, dtype=torch.bfloat16)
+    q = wv.qkv_project(plan, desc, t, cache, x, torch.from_numpy(w).to(device=gpu_device, dtype=torch.bfloat16),
+                       x_layout=layout)
+    torch.cuda.synchronize()
+    q = q.float().cpu().numpy()
+    k_all = cache.k.float().cpu().numpy()
+    vt_all = cache.vt.float().cpu().numpy()
+    lpad = plan.lpad()
+    written = set()
+    for n in nodes:
+        a = a_of[(n[0], n[1])].astype(np.float64)
+        qo, ko, vo = oc.project(a, w.astype(np.float64), heads, hd)
+        inv = 1.0 / np.sqrt(np.mean(a * a, axis=1) + 1e-6)
+        acc_err = (D * 2.0 ** -24) * (np.abs(a) @ np.abs(w.astype(np.float64)).T) * inv[:, None]
+        acc_q, acc_k, acc_v = (acc_err[:, i * D:(i + 1) * D].reshape(-1, heads, hd) for i in range(3))
+        ctx = plan.node_ctx(n)  # own slot last
+        phys = int(ctx[-1][2])
+        written.add(phys)
+        for name, got, ref, acc in (("q", q[n[4]:n[4] + n[5]], qo, acc_q),
+                                    ("k", k_all[phys][:, :L].transpose(1, 0, 2), ko, acc_k),
+                                    ("v", vt_all[phys][:, :, :L].transpose(2, 0, 1), vo, acc_v)):
+            err = np.abs(got - ref)
+            bound = 2.0 ** -7 * (np.abs(ref) + acc) + acc
+            assert (err <= bound).all(), f"node {(n[0], n[1])} {name}: worst {err.max()}"
+        assert (k_all[phys][:, L:] == 0).all() and (vt_all[phys][:, :, L:] == 0).all()
+    for s in range(plan.num_phys_slots):
+        if s not in written:
+            assert np.isnan(k_all[s]).all() and np.isnan(vt_all[s]).all(), f"slot {s} written"
+
+
+def test_chain_store_copies_node_rows(gpu_device):
+    import torch
+    L, D = 96, 128
+    plan = wv.wave_plan(B=4, K=2, policy=wi.SAME_LEVEL, sched=wv.WAVE, chunk_len=L)
+    desc = plan.upload(gpu_device)
+    t = 3
+    rows = int(plan.round_q_rows[t])
+    o = torch.arange(rows * D, device=gpu_device, dtype=torch.float32).remainder(251).to(torch.bfloat16).view(rows, D)
+    state = torch.full((4, L, D), -1.0, device=gpu_device, dtype=torch.bfloat16)
+    wv.chain_store(plan, desc, t, o, state)
+    torch.cuda.synchronize()
+    seen = set()
+    for n in plan.round_nodes(t).tolist():
+        assert torch.equal(state[n[0]], o[n[4]:n[4] + n[5]])
+        seen.add(n[0])
+    for c in range(4):
+        if c not in seen:
+            assert (state[c] == -1).all()
+
+
+CHAIN_GRID = [
+    # policy, B, K, L, heads, hd, layers
+    (wi.PROGRESSIVE, 3, 2, 160, 2, 64, 2),
+    (wi.SAME_LEVEL, 4, 2, 130, 1, 128, 1),
+    (wi.CLEAN, 3, 3, 96, 2, 64, 2),
+]
+
+
+@pytest.mark.parametrize("policy,B,K,L,heads,hd,layers", CHAIN_GRID)
+def test_chain_matches_oracle(gpu_device, policy, B, K, L, heads, hd, layers):
+    """Every node's per-layer attention output of a whole chain against the
+    independent fp64 chain oracle."""
+    noise, weights = _inputs(40 + L, B, L, heads, hd, layers)
+    scale = 1.0 / math.sqrt(hd)
+    plan = wv.wave_plan(B=B, K=K, policy=policy, sched=wv.WAVE, chunk_len=L)
+    log(f"chain policy={policy} B={B} K={K} L={L} heads={heads} hd={hd} layers={layers}")
+    got = gpu_chain(plan, B, L, heads, hd, noise, weights, scale, gpu_device)
+    p = op.Params(B, K, policy, op.SERIAL, -1, L, 0, 0)
+    ref = oc.chain_rollout(p, op.oracle_plan(p), layers, heads, hd, lambda c: noise[c].astype(np.float64),
+                           lambda l: weights[l].astype(np.float64), scale)
+    assert set(got) == set(ref)
+    worst = 0.0
+    for key, (_, per_layer) in ref.items():
+        for layer, (g, r) in enumerate(zip(got[key], per_layer)):
+            rel = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30))
+            worst = max(worst, rel)
+            assert np.isfinite(g).all()
+            assert rel <= CHAIN_REL_FRO, f"node {key} layer {layer}: rel {rel}"
+    log(f"  worst relative Frobenius error {worst:.3g}")
+
+
+# Bound for whole chains, relative Frobenius norm per node and layer.  One
+# stage (projection, then attention) adds at most e = 3e-3: two bf16 roundings
+# (Q/K/V and O, each 2^-9 relative at worst, about 2^-9/sqrt(3) in RMS) plus
+# the attention's own fp32/bf16 error (about 1e-3 at these sizes).  An input
+# error grows by at most g = 1.5 through a stage: the projection is
+# RMS-normalised, and the softmax of unit-variance scaled scores changes its
+# weights by at most about half the relative change of the scores.  The
+# deepest stage in CHAIN_GRID is the 6th (3 levels x 2 layers), so
+# e * (g^6 - 1) / (g - 1) = 6.2e-2.
+CHAIN_REL_FRO = 6e-2
+
+
+@pytest.mark.parametrize("policy", [wi.CLEAN, wi.SAME_LEVEL, wi.PROGRESSIVE])
+def test_chain_serial_equals_wave_bitwise(gpu_device, policy):
+    """Real data flow through the schedule: serial and pipelined rounds give
+    bitwise identical outputs for every node and layer."""
+    B, K, L, heads, hd, layers = 4, 3, 200, 2, 64, 2
+    noise, weights = _inputs(77, B, L, heads, hd, layers)
+    outs = {}
+    for sched in (wv.SERIAL, wv.WAVE):
+        plan = wv.wave_plan(B=B, K=K, policy=policy, sched=sched, chunk_len=L)
+        outs[sched] = gpu_chain(plan, B, L, heads, hd, noise, weights, 0.125, gpu_device)
+    assert set(outs[wv.SERIAL]) == set(outs[wv.WAVE])
+    for key in outs[wv.WAVE]:
+        for a, b in zip(outs[wv.SERIAL][key], outs[wv.WAVE][key]):
+            assert np.array_equal(a, b), key

@@ -115,7 +115,7 @@ def test_work_list_covers_nodes_and_is_sorted():
 def test_descriptor_layout():
     pn = native(5, 3, op.PROGRESSIVE, op.WAVE, 2, 100, 7)
     d = pn.desc()
-    assert d[0] == 0x57415645 and d[1] == 1
+    assert d[0] == 0x57415645 and d[1] == 2
     nr, nn, nc, nw, nk = d[2:7]
     assert (nr, nn, nc, nw, nk) == (pn.num_rounds, len(pn.nodes), len(pn.ctx), len(pn.writes), len(pn.work))
     off_r, off_n, off_c, off_w, off_k = d[7:12]
@@ -123,8 +123,9 @@ def test_descriptor_layout():
     assert rt[:, 0].tolist() == pn.round_node_begin[:-1].tolist()
     assert rt[:, 6].tolist() == pn.round_q_rows.tolist()
     assert rt[:, 7].tolist() == pn.round_src_rows.tolist()
-    nt = d[off_n:off_n + 4 * nn].reshape(nn, 4)
+    nt = d[off_n:off_n + 6 * nn].reshape(nn, 6)
     assert (nt[:, 0] == pn.nodes[:, 4]).all() and (nt[:, 3] == pn.nodes[:, 7]).all()
+    assert (nt[:, 4] == pn.nodes[:, 0]).all() and (nt[:, 5] == pn.nodes[:, 1]).all()
     ct = d[off_c:off_c + 2 * nc].reshape(nc, 2)
     assert (ct[:, 0] == pn.ctx[:, 2]).all() and (ct[:, 1] == pn.ctx[:, 3]).all()
     wt = d[off_w:off_w + 4 * nw].reshape(nw, 4)
