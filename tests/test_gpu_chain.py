@@ -191,3 +191,77 @@ def test_chain_serial_equals_wave_bitwise(gpu_device, policy):
     for key in outs[wv.WAVE]:
         for a, b in zip(outs[wv.SERIAL][key], outs[wv.WAVE][key]):
             assert np.array_equal(a, b), key
+
+
+def _device_chain(plan, w, layers, device, policy):
+    """Full-size chain on the device; returns {(chunk, level): last-layer O (bf16, on the device)}."""
+    import torch
+    D = w.heads * w.head_dim
+    desc = plan.upload(device)
+    caches = [wv.KVCache(plan.num_phys_slots, w.heads, w.head_dim, plan.lpad(), device, fill=float("nan"))
+              for _ in range(layers)]
+    weights = [wi.device_chain_weight(w.key, l, D, device) for l in range(layers)]
+    state = torch.stack([wi.device_chain_noise(w.key, c, w.chunk_len, D, device) for c in range(w.B)])
+    outs = {}
+    for t in range(plan.num_rounds):
+        rows = int(plan.round_q_rows[t])
+        x, layout = state, wv.X_CHUNK
+        for layer in range(layers):
+            q = wv.qkv_project(plan, desc, t, caches[layer], x, weights[layer], x_layout=layout)
+            o, _ = wv.wave_attn(plan, desc, t, caches[layer], q, w.scale, want_lse=False, balance=False)
+            x, layout = o.view(rows, D), wv.X_ROUND
+        wv.chain_store(plan, desc, t, o, state)
+        for n in plan.round_nodes(t).tolist():
+            outs[(n[0], n[1])] = o[n[4]:n[4] + n[5]].clone()
+    torch.cuda.synchronize()
+    return outs
+
+
+def test_chain_full_size_serial_equals_wave(gpu_device):
+    """The 832x480 seven-chunk K=5 shape (4680 tokens, 12 heads x 128), two
+    layers, progressive: serial (35 rounds) and pipelined (11 rounds) chains
+    give bitwise identical outputs for every node."""
+    import torch
+    w = wi.WORKLOADS[3]
+    outs = {}
+    for sched in (wv.SERIAL, wv.WAVE):
+        plan = wv.wave_plan(B=w.B, K=w.K, policy=wi.PROGRESSIVE, sched=sched, chunk_len=w.chunk_len)
+        log(f"full-size chain, sched={sched}: {plan.num_rounds} rounds")
+        outs[sched] = _device_chain(plan, w, 2, gpu_device, wi.PROGRESSIVE)
+    assert set(outs[wv.SERIAL]) == set(outs[wv.WAVE]) and len(outs[wv.WAVE]) >= w.B * w.K
+    for key, o in outs[wv.WAVE].items():
+        assert torch.equal(o, outs[wv.SERIAL][key]), key
+        assert torch.isfinite(o.float()).all()
+
+
+def test_qkv_project_full_size_sampled(gpu_device):
+    """qkv_project of the 832x480 K=4 round 6 (5 nodes x 4680 tokens, D = 1536)
+    on the chunks' seeded noise: 48 sampled rows of every node against
+    oracle.chain.project, and every written slot's tail exactly zero."""
+    import torch
+    w = wi.WORKLOADS[2]
+    D = w.heads * w.head_dim
+    plan = wv.wave_plan(B=w.B, K=w.K, policy=wi.PROGRESSIVE, sched=wv.WAVE, chunk_len=w.chunk_len)
+    desc = plan.upload(gpu_device)
+    cache = wv.KVCache(plan.num_phys_slots, w.heads, w.head_dim, plan.lpad(), gpu_device, fill=float("nan"))
+    state = torch.stack([wi.device_chain_noise(w.key, c, w.chunk_len, D, gpu_device) for c in range(w.B)])
+    wt = wi.device_chain_weight(w.key, 0, D, gpu_device)
+    q = wv.qkv_project(plan, desc, w.round, cache, state, wt, x_layout=wv.X_CHUNK)
+    torch.cuda.synchronize()
+    w64 = wt.float().cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(3)
+    for n in plan.round_nodes(w.round).tolist():
+        rows = np.unique(np.concatenate([[0, w.chunk_len - 1], rng.integers(0, w.chunk_len, 46)]))
+        a = state[n[0]][rows].float().cpu().numpy().astype(np.float64)
+        qo, ko, vo = oc.project(a, w64, w.heads, w.head_dim)
+        inv = 1.0 / np.sqrt(np.mean(a * a, axis=1) + 1e-6)
+        acc = (D * 2.0 ** -24) * (np.abs(a) @ np.abs(w64).T) * inv[:, None]
+        phys = int(plan.node_ctx(n)[-1][2])
+        got_q = q[n[4] + rows].float().cpu().numpy()
+        got_k = cache.k[phys][:, rows].float().cpu().numpy().transpose(1, 0, 2)
+        got_v = cache.vt[phys][:, :, rows].float().cpu().numpy().transpose(2, 0, 1)
+        for i, (got, ref) in enumerate(((got_q, qo), (got_k, ko), (got_v, vo))):
+            ac = acc[:, i * D:(i + 1) * D].reshape(len(rows), w.heads, w.head_dim)
+            assert (np.abs(got - ref) <= 2.0 ** -7 * (np.abs(ref) + ac) + ac).all(), (n[0], n[1], "qkv"[i])
+        lp = plan.lpad()
+        assert (cache.k[phys][:, w.chunk_len:lp] == 0).all() and (cache.vt[phys][:, :, w.chunk_len:lp] == 0).all()

@@ -254,3 +254,43 @@ def test_tail_balancing_choice_and_workspace_checks():
     if dev_cus.value > 0:
         assert attn(C.c_void_p(0x10100), dev_cus.value - 1) == _lib.WAVE_ERR_CAPACITY
     assert attn(C.c_void_p(0x10010), 1 << 40) == _lib.WAVE_ERR_INVALID_ARG
+
+
+def test_chain_calls_validate_before_launch():
+    """qkv_project / chain_store reject bad arguments on the host (no GPU needed)."""
+    lib = _lib.load()
+    pn = native(4, 2, op.PROGRESSIVE, op.WAVE, -1, 128, 0)
+    fake = C.c_void_p(0x10000)
+    ws = C.c_void_p(0x20000)
+    cache = _lib.KvCache(0x10000, 0x20000, pn.num_phys_slots, 2, 64, pn.lpad())
+    stream = C.c_void_p(0)
+    b = C.c_size_t()
+    assert lib.qkv_project_workspace(pn.handle, 1, C.byref(b)) == 0
+    assert b.value == int(pn.round_q_rows[1]) * 4
+    assert lib.qkv_project_workspace(pn.handle, 99, C.byref(b)) == _lib.WAVE_ERR_INVALID_ARG
+
+    def proj(plan=pn, round_=1, cache_=cache, x=fake, layout=0, w=fake, q=fake, wsp=ws, nbytes=1 << 20):
+        return lib.qkv_project(plan.handle, fake, round_, C.byref(cache_), x, layout, w, q, wsp, nbytes, stream)
+
+    assert proj(round_=9) == _lib.WAVE_ERR_INVALID_ARG
+    assert proj(x=None) == _lib.WAVE_ERR_INVALID_ARG
+    assert proj(layout=2) == _lib.WAVE_ERR_INVALID_ARG
+    assert proj(q=C.c_void_p(0x10008)) == _lib.WAVE_ERR_UNSUPPORTED
+    assert proj(wsp=None) == _lib.WAVE_ERR_INVALID_ARG
+    assert proj(nbytes=4) == _lib.WAVE_ERR_CAPACITY
+    assert proj(cache_=_lib.KvCache(0x10000, 0x20000, pn.num_phys_slots, 1, 64, pn.lpad())) \
+        == _lib.WAVE_ERR_UNSUPPORTED  # D = 64 is not a multiple of 128
+    with_cond = native(4, 2, op.PROGRESSIVE, op.WAVE, -1, 128, 16)
+    c2 = _lib.KvCache(0x10000, 0x20000, with_cond.num_phys_slots, 2, 64, with_cond.lpad())
+    assert proj(plan=with_cond, cache_=c2) == _lib.WAVE_ERR_UNSUPPORTED
+    short_q = native(4, 2, op.PROGRESSIVE, op.WAVE, -1, 128, 0, query_len=32)
+    assert proj(plan=short_q) == _lib.WAVE_ERR_UNSUPPORTED
+
+    def store(plan=pn, round_=1, dim=128, o=fake, st=fake):
+        return lib.chain_store(plan.handle, fake, round_, dim, o, st, stream)
+
+    assert store(round_=-1) == _lib.WAVE_ERR_INVALID_ARG
+    assert store(dim=12) == _lib.WAVE_ERR_INVALID_ARG
+    assert store(st=None) == _lib.WAVE_ERR_INVALID_ARG
+    assert store(o=C.c_void_p(0x10004)) == _lib.WAVE_ERR_UNSUPPORTED
+    assert store(plan=with_cond) == _lib.WAVE_ERR_UNSUPPORTED
