@@ -407,8 +407,9 @@ int32_t qkv_project(const wave_plan_t* plan, const void* d_desc, int32_t round, 
   if (workspace_bytes < static_cast<size_t>(p.round_q_rows[round]) * sizeof(float))
     return set_error(WAVE_ERR_CAPACITY, f + ": workspace smaller than qkv_project_workspace()");
   const int32_t n0 = p.round_node_begin[round], n1 = p.round_node_begin[round + 1];
-  const int32_t row_tiles = (cache->lpad + 127) / 128;
-  const int32_t col_tiles = static_cast<int32_t>(3 * D / 128);
+  const int32_t row_tiles = (cache->lpad + wave::kProjTileRows - 1) / wave::kProjTileRows;
+  const int32_t col_tiles = static_cast<int32_t>(3 * D / wave::kProjTileCols);
+  static_assert(wave::kProjTileCols == 128, "D must be a multiple of the column tile");
   if (static_cast<int64_t>(n1 - n0) * row_tiles * col_tiles > INT32_MAX ||
       static_cast<int64_t>(p.params.chunk_len) * D * 2 > UINT32_MAX)
     return set_error(WAVE_ERR_UNSUPPORTED, f + ": too many workgroups or chunk rows too large");

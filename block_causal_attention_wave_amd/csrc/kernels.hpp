@@ -59,6 +59,9 @@ struct AttnArgs {
   float* part_lse;
 };
 
+// Output tile of one qkv_project workgroup: tokens x projection columns.
+constexpr int kProjTileRows = 256, kProjTileCols = 128;
+
 // Toy-chain QKV projection of one round at one layer: every node's input
 // rows x (round-packed [round rows][D], or per-chunk state [chunks][chunk_rows][D]
 // when x_chunk) times W^T ([3D][D]), scaled per row by 1/rms (row_scale,

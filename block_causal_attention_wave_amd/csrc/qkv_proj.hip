@@ -13,11 +13,13 @@
 //
 // Kernels:
 //   row_scale_kernel  1 / rms of every input row (one wave per row).
-//   qkv_gemm_kernel   one workgroup per (node, 128-token tile, 128-column
-//                     tile): bf16 MFMA 32x32x16, fp32 accumulation, a
-//                     two-stage LDS ring of 128x64 A and W tiles filled by
-//                     direct global->LDS loads, and an epilogue that scales,
-//                     rounds and scatters the tile through LDS.
+//   qkv_gemm_kernel   one workgroup per (node, 256-token tile, 128-column
+//                     tile), 8 waves of 64x64: bf16 MFMA 32x32x16, fp32
+//                     accumulation, a three-stage LDS ring of 256x64 A and
+//                     128x64 W tiles filled by direct global->LDS loads (two
+//                     k-steps in flight, one barrier per k-step), and an
+//                     epilogue that scales, rounds and scatters the tile
+//                     through LDS.
 //   chain_store_kernel  copies each node's output rows to its chunk's state.
 #include <hip/hip_runtime.h>
 
@@ -32,15 +34,21 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int TM = 128, TN = 128, TK = 64;
-constexpr int THREADS = 256;
-constexpr int ROW_BYTES = TK * 2;            // one tile row in LDS
-constexpr int TILE_BYTES = TM * ROW_BYTES;   // 16 KiB (A and W tiles alike)
-constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // A tile then W tile
-constexpr int LOADS = TILE_BYTES / (THREADS * 16);  // 16-byte loads per thread per tile
-constexpr int OUT_PITCH = (TN + 8) * 2;      // bytes per row of the staged output tile
-static_assert(TM == TN, "A and W tiles share one layout");
-static_assert(TM * OUT_PITCH <= 2 * STAGE_BYTES, "the output tile fits in the ring");
+constexpr int TM = kProjTileRows, TN = kProjTileCols, TK = 64;
+constexpr int WAVES = 8;
+constexpr int THREADS = 64 * WAVES;
+constexpr int NSTAGE = 3;
+constexpr int ROW_BYTES = TK * 2;              // one tile row in LDS
+constexpr int A_BYTES = TM * ROW_BYTES;        // 32 KiB
+constexpr int W_BYTES = TN * ROW_BYTES;        // 16 KiB
+constexpr int STAGE_BYTES = A_BYTES + W_BYTES;  // A tile then W tile
+constexpr int A_LOADS = A_BYTES / (THREADS * 16);  // 16-byte loads per thread per A tile
+constexpr int W_LOADS = W_BYTES / (THREADS * 16);
+constexpr int OUT_PITCH_R = (TN + 8) * 2;      // row-major staging: bytes per token row
+constexpr int OUT_PITCH_C = (TM + 8) * 2;      // column-major staging: bytes per column
+static_assert(TM == 4 * 64 && TN == 2 * 64, "8 waves of 64x64");
+static_assert(TM * OUT_PITCH_R <= NSTAGE * STAGE_BYTES && TN * OUT_PITCH_C <= NSTAGE * STAGE_BYTES,
+              "the staged output tile fits in the ring");
 
 // 16-byte chunk swizzle of a 128-byte LDS row: a 16-byte LDS read is served
 // 16 lanes at a time (a half-wave's lane quads of equal index parity), and an
@@ -70,15 +78,37 @@ __global__ __launch_bounds__(256) void row_scale_kernel(ProjArgs a) {
 
 template <int HD>
 __global__ __launch_bounds__(THREADS, 2) void qkv_gemm_kernel(ProjArgs a) {
-  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wr = wv >> 1, wc = wv & 1;  // this wave's 64x64 quarter of the tile
+  const int wr = wv >> 1, wc = wv & 1;  // this wave's 64x64 block of the tile
+  // Tile order.  The dispatcher hands workgroup i to XCD i % 8; each XCD has
+  // its own L2.  Remap so that every XCD runs a contiguous range of tiles,
+  // and within a node order them by groups of 4 row tiles x all column
+  // tiles (row tile fastest): the ~32 workgroups an XCD runs at once then
+  // cover 4 A row tiles x 8 W column tiles and share their k-slices in L2.
   int b = blockIdx.x;
-  const int ct = b % a.col_tiles;
-  b /= a.col_tiles;
-  const int rt = b % a.row_tiles;
-  const int node = a.node_begin + b / a.row_tiles;
+  {
+    const int per_xcd = (int)(gridDim.x / 8);
+    if (b < per_xcd * 8) b = (b % 8) * per_xcd + b / 8;
+  }
+  const int per_node = a.row_tiles * a.col_tiles;
+  const int node = a.node_begin + b / per_node;
+  int rt, ct;
+  {
+    constexpr int G = 4;
+    const int r = b % per_node;
+    const int full = a.row_tiles / G;
+    const int gsz = G * a.col_tiles;
+    if (r < full * gsz) {
+      ct = (r % gsz) / G;
+      rt = (r / gsz) * G + r % G;
+    } else {
+      const int rem = a.row_tiles - full * G, rr = r - full * gsz;
+      ct = rr / rem;
+      rt = full * G + rr % rem;
+    }
+  }
   const int32_t* nd = a.nodes + kDescNodeWords * node;
   const int q_offset = nd[0], L = nd[1], chunk = nd[4];
   const int phys = a.ctx[2 * (nd[2] + nd[3] - 1)];  // the node's own slot: last in its gather list
@@ -90,24 +120,30 @@ __global__ __launch_bounds__(THREADS, 2) void qkv_gemm_kernel(ProjArgs a) {
   const char* abase = static_cast<const char*>(a.x) +
                       ((a.x_chunk ? (int64_t)chunk * a.chunk_rows : (int64_t)q_offset) * D) * 2;
   const char* wbase = static_cast<const char*>(a.w) + (int64_t)c0 * D * 2;
-  uint32_t aoff[LOADS], woff[LOADS];
+  uint32_t aoff[A_LOADS], woff[W_LOADS];
 #pragma unroll
-  for (int n = 0; n < LOADS; ++n) {
-    const int off = (wv * LOADS + n) * 1024 + lane * 16;
+  for (int n = 0; n < A_LOADS; ++n) {
+    const int off = (wv * A_LOADS + n) * 1024 + lane * 16;
     const int row = off / ROW_BYTES;
     const int lc = ((off % ROW_BYTES) / 16) ^ swz(row);
     aoff[n] = (uint32_t)(((int64_t)min(r0 + row, L - 1) * D + lc * 8) * 2);
+  }
+#pragma unroll
+  for (int n = 0; n < W_LOADS; ++n) {
+    const int off = (wv * W_LOADS + n) * 1024 + lane * 16;
+    const int row = off / ROW_BYTES;
+    const int lc = ((off % ROW_BYTES) / 16) ^ swz(row);
     woff[n] = (uint32_t)(((int64_t)row * D + lc * 8) * 2);
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
   auto issue = [&](int ks, int stage) {
     const char* ab = abase + (int64_t)ks * TK * 2;
     const char* wb = wbase + (int64_t)ks * TK * 2;
-    const uint32_t sa = lds0 + stage * STAGE_BYTES, sw = sa + TILE_BYTES;
+    const uint32_t sa = lds0 + stage * STAGE_BYTES, sw = sa + A_BYTES;
 #pragma unroll
-    for (int n = 0; n < LOADS; ++n) load_lds16(sa + (wv * LOADS + n) * 1024, ab, aoff[n]);
+    for (int n = 0; n < A_LOADS; ++n) load_lds16(sa + (wv * A_LOADS + n) * 1024, ab, aoff[n]);
 #pragma unroll
-    for (int n = 0; n < LOADS; ++n) load_lds16(sw + (wv * LOADS + n) * 1024, wb, woff[n]);
+    for (int n = 0; n < W_LOADS; ++n) load_lds16(sw + (wv * W_LOADS + n) * 1024, wb, woff[n]);
   };
   auto barrier = [&]() {
     asm volatile("" ::: "memory");
@@ -124,21 +160,25 @@ __global__ __launch_bounds__(THREADS, 2) void qkv_gemm_kernel(ProjArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+  // Three-stage ring: k-steps ks and ks+1 in flight while ks is consumed;
+  // k-step ks+2 goes into the stage k-step ks-1 used, after the barrier that
+  // every wave passes only once done with ks-1.
   const int nk = D / TK;
+  constexpr int TILE_LOADS = A_LOADS + W_LOADS;
+  static_assert(TILE_LOADS <= 15, "vmcnt immediate");
   issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  int stage = 0;
   for (int ks = 0; ks < nk; ++ks) {
-    if (ks + 1 < nk) {
-      issue(ks + 1, (ks + 1) & 1);
-      __builtin_amdgcn_s_waitcnt(kWaitExp | (2 * LOADS));  // this step's tiles have landed
-    } else {
-      __builtin_amdgcn_s_waitcnt(kWaitExp);
-    }
+    if (ks + 1 < nk) __builtin_amdgcn_s_waitcnt(kWaitExp | TILE_LOADS);  // k-step ks has landed
+    else __builtin_amdgcn_s_waitcnt(kWaitExp);
     barrier();
-    const char* sa = lds + (ks & 1) * STAGE_BYTES;
-    const char* sw = sa + TILE_BYTES;
-#pragma unroll
-    for (int s = 0; s < TK / 16; ++s) {
-      bf16x8 af[2], bf[2];
+    if (ks + 2 < nk) issue(ks + 2, stage == 0 ? 2 : stage - 1);
+    const char* sa = lds + stage * STAGE_BYTES;
+    const char* sw = sa + A_BYTES;
+    // Operand fragments of 16-deep substep s+1 are read while the MFMAs of
+    // substep s run.
+    auto frags = [&](int s, bf16x8 (&af)[2], bf16x8 (&bf)[2]) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int row = wr * 64 + i * 32 + (lane & 31);
@@ -149,13 +189,29 @@ __global__ __launch_bounds__(THREADS, 2) void qkv_gemm_kernel(ProjArgs a) {
         const int row = wc * 64 + j * 32 + (lane & 31);
         bf[j] = *reinterpret_cast<const bf16x8*>(sw + row * ROW_BYTES + (((2 * s + (lane >> 5)) ^ swz(row)) * 16));
       }
+    };
+    bf16x8 af[2][2], bf[2][2];
+    frags(0, af[0], bf[0]);
+#pragma unroll
+    for (int s = 0; s < TK / 16; ++s) {
+      if (s + 1 < TK / 16) frags(s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][i], bf[s & 1][j], acc[i][j], 0, 0, 0);
     }
-    barrier();  // the next issue overwrites this stage
+    // Keep that order: reads of substeps 0 and 1, then (MFMAs of s, reads of s+2).
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int s = 0; s < TK / 16 - 2; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    stage = stage == NSTAGE - 1 ? 0 : stage + 1;
   }
+  barrier();  // the epilogue reuses the ring
 
   // Epilogue: scale rows by 1/rms (0 past the chunk's tokens), round to bf16
   // and stage the tile in LDS: row-major for Q and K columns, column-major
@@ -180,11 +236,11 @@ __global__ __launch_bounds__(THREADS, 2) void qkv_gemm_kernel(ProjArgs a) {
           bf16x4 v;
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[i][j][4 * g + e] * sc[e]);
-          *reinterpret_cast<bf16x4*>(lds + col * OUT_PITCH + row0 * 2) = v;
+          *reinterpret_cast<bf16x4*>(lds + col * OUT_PITCH_C + row0 * 2) = v;
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            *reinterpret_cast<__bf16*>(lds + (row0 + e) * OUT_PITCH + col * 2) = (__bf16)(acc[i][j][4 * g + e] * sc[e]);
+            *reinterpret_cast<__bf16*>(lds + (row0 + e) * OUT_PITCH_R + col * 2) = (__bf16)(acc[i][j][4 * g + e] * sc[e]);
         }
       }
     }
@@ -195,14 +251,14 @@ __global__ __launch_bounds__(THREADS, 2) void qkv_gemm_kernel(ProjArgs a) {
     if (part == 2) {
       const int col = id / (TM / 8), tok = r0 + (id % (TM / 8)) * 8;
       if (tok >= lpad) continue;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + col * OUT_PITCH + (tok - r0) * 2);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + col * OUT_PITCH_C + (tok - r0) * 2);
       const int h = (c0 - 2 * D + col) / HD, dd = (c0 - 2 * D + col) % HD;
       __bf16* dst = static_cast<__bf16*>(a.vt) + (((int64_t)phys * heads + h) * HD + dd) * lpad + tok;
       *reinterpret_cast<u32x4*>(dst) = v;
     } else {
       const int row = id / (TN / 8), cc = (id % (TN / 8)) * 8;
       const int r = r0 + row;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * OUT_PITCH + cc * 2);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * OUT_PITCH_R + cc * 2);
       if (part == 0) {
         if (r >= L) continue;
         __bf16* dst = static_cast<__bf16*>(a.q) + (int64_t)(q_offset + r) * D + c0 + cc;

@@ -378,3 +378,21 @@ def test_tail_balancing_matches_unbalanced(gpu_device):
         f"lse max {np.abs(l0[:, cut] - l1[:, cut]).max():.3g}")
     assert d.max() <= MAX_ABS and d.mean() <= MEAN_ABS
     assert np.abs(l0[:, cut] - l1[:, cut]).max() <= LSE_ABS
+
+
+def test_longest_gather_lists(gpu_device):
+    """512 chunks with clean history (K=1): the last updates read 512 slots, the
+    longest gather list the kernels stage.  The whole 1023-round rollout runs
+    on the GPU; the last four nodes are checked against the oracle."""
+    B, K, L, heads, hd = 512, 1, 16, 1, 64
+    plan = wv.wave_plan(B=B, K=K, policy=wi.CLEAN, sched=wv.WAVE, chunk_len=L)
+    assert int(plan.nodes[:, 7].max()) == 512
+    log(f"longest gather lists: {plan.num_rounds} rounds")
+    inp = HostInputs(512, heads, hd, L, 0, bf16=True)
+    scale = 1.0 / np.sqrt(hd)
+    got = gpu_rollout(plan, inp, gpu_device, scale, src_dtype="bf16", balance=False)
+    want = {(c, 1) for c in range(B - 4, B)}
+    ref = oracle_rollout(B, K, wi.CLEAN, -1, L, 0, inp, scale, want=want)
+    assert want <= set(ref)
+    for key in want:
+        compare(got[key][0], got[key][1], ref[key][0], ref[key][1], f"node {key}")

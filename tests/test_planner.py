@@ -294,3 +294,22 @@ def test_chain_calls_validate_before_launch():
     assert store(st=None) == _lib.WAVE_ERR_INVALID_ARG
     assert store(o=C.c_void_p(0x10004)) == _lib.WAVE_ERR_UNSUPPORTED
     assert store(plan=with_cond) == _lib.WAVE_ERR_UNSUPPORTED
+
+
+def test_attention_rejects_gather_lists_past_512_slots():
+    """The kernels stage a node's gather list in LDS, 512 slots at most: a plan
+    whose longest list is 513 slots (513 chunks, clean history) is rejected on
+    the host; 512 is accepted by the plan-level checks."""
+    lib = _lib.load()
+    fake = C.c_void_p(0x10000)
+    for B, want in ((513, _lib.WAVE_ERR_UNSUPPORTED), (512, None)):
+        pn = native(B, 1, op.CLEAN, op.WAVE, -1, 16, 0)
+        assert int(pn.nodes[:, 7].max()) == B
+        cache = _lib.KvCache(0x10000, 0x20000, pn.num_phys_slots, 1, 64, pn.lpad())
+        misaligned_o = C.c_void_p(0x10008)  # fails a later host check, so nothing is launched
+        rc = lib.wave_attn(pn.handle, fake, 0, C.byref(cache), fake, 0, 64, misaligned_o, None, 0.125,
+                           None, 0, C.c_void_p(0))
+        if want is not None:
+            assert rc == want and b"512" in lib.wave_last_error()
+        else:
+            assert rc == _lib.WAVE_ERR_UNSUPPORTED and b"aligned" in lib.wave_last_error()
