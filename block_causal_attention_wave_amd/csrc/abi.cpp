@@ -176,14 +176,10 @@ int32_t device_cus() {
   return cus;
 }
 
-// Splits for split-KV attention: enough workgroups for about two per compute
-// unit, at most 64 splits.
-int32_t auto_splits(const wave::Plan& p, int32_t round, int32_t heads) {
-  const int32_t cus = device_cus();
-  const int64_t items = static_cast<int64_t>(p.round_work_begin[round + 1] - p.round_work_begin[round]) * heads;
-  if (items <= 0) return 1;
-  int64_t s = (2 * static_cast<int64_t>(cus) + items - 1) / items;
-  return static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(s, 64)));
+// Splits for split-KV attention: the count whose simulated dispatch onto the
+// current device's compute units finishes first (merge included), 1..64.
+int32_t auto_splits(const wave::Plan& p, int32_t round, int32_t heads, int32_t head_dim) {
+  return wave::choose_splits(p, round, heads, head_dim, device_cus());
 }
 
 constexpr size_t kAlign = 256;
@@ -328,7 +324,7 @@ int32_t wave_attn_splitkv_workspace(const wave_plan_t* plan, int32_t round, int3
     return set_error(WAVE_ERR_INVALID_ARG, "wave_attn_splitkv_workspace: round out of range");
   if (heads < 1 || head_dim < 1 || num_splits < 0 || num_splits > 4096)
     return set_error(WAVE_ERR_INVALID_ARG, "wave_attn_splitkv_workspace: bad heads, head_dim or num_splits");
-  const int32_t s = num_splits == 0 ? auto_splits(p, round, heads) : num_splits;
+  const int32_t s = num_splits == 0 ? auto_splits(p, round, heads, head_dim) : num_splits;
   *bytes = splitkv_bytes(p, round, heads, head_dim, s, nullptr);
   if (splits_used) *splits_used = s;
   return ok();
@@ -344,7 +340,7 @@ int32_t wave_attn_splitkv(const wave_plan_t* plan, const void* d_desc, int32_t r
   if (num_splits < 0 || num_splits > 4096)
     return set_error(WAVE_ERR_INVALID_ARG, "wave_attn_splitkv: num_splits must be in [0, 4096]");
   const wave::Plan& p = plan->p;
-  const int32_t s = num_splits == 0 ? auto_splits(p, round, cache->heads) : num_splits;
+  const int32_t s = num_splits == 0 ? auto_splits(p, round, cache->heads, cache->head_dim) : num_splits;
   size_t lse_off = 0;
   const size_t need = splitkv_bytes(p, round, cache->heads, cache->head_dim, s, &lse_off);
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)

@@ -61,6 +61,26 @@ double simulate_round(const Plan& p, int32_t round, int32_t heads, int32_t cus, 
   return simulate(item_tiles(p, round), heads, std::max(cus, 1), t);
 }
 
+int32_t choose_splits(const Plan& p, int32_t round, int32_t heads, int32_t head_dim, int32_t cus) {
+  const std::vector<int64_t> tiles = item_tiles(p, round);
+  const int32_t n = static_cast<int32_t>(tiles.size());
+  if (n == 0 || heads < 1 || cus < 1) return 1;
+  const double tile_s = kTileSeconds * head_dim / 128.0;
+  const double rows = static_cast<double>(p.round_q_rows[round]);
+  int32_t best = 1;
+  double best_t = 0.0;
+  for (int32_t s = 1; s <= 64; ++s) {
+    const TailSplit t{n, s};
+    double v = simulate(tiles, heads, cus, t);
+    if (s > 1) v += (static_cast<double>(s) * rows * heads * head_dim * 4.0 / kMergeBytesPerSecond + kLaunchSeconds) / tile_s;
+    if (s == 1 || v < best_t) {
+      best_t = v;
+      best = s;
+    }
+  }
+  return best;
+}
+
 TailSplit choose_tail_split(const Plan& p, int32_t round, int32_t heads, int32_t head_dim, int32_t cus) {
   const std::vector<int64_t> tiles = item_tiles(p, round);
   const int32_t n = static_cast<int32_t>(tiles.size());

@@ -24,6 +24,11 @@ struct TailSplit {
 // shortens the simulated round).
 TailSplit choose_tail_split(const Plan& p, int32_t round, int32_t heads, int32_t head_dim, int32_t cus);
 
+// Key splits for split-KV attention of `round` (every work item cut into
+// that many ranges), 1..64: the count with the shortest simulated round,
+// merge pass included.
+int32_t choose_splits(const Plan& p, int32_t round, int32_t heads, int32_t head_dim, int32_t cus);
+
 // Simulated duration, in key-tile times, of the round with that split: each
 // workgroup costs its key tiles plus a fixed start-up; pieces pay a partial
 // result write as well.  The merge pass is not included.
