@@ -21,8 +21,8 @@ What it computes, and where the pages fix it
   block-causal timeline and feeds language/state to the generator only as a
   K/V slice.
 
-Readings where the pages are silent (each is listed in the design doc)
-------------------------------------------------------------------
+Readings where the pages are silent
+-----------------------------------
 * Level 0 is the clean (fully denoised) state, level K pure noise.  Update
   U(i, j) consumes chunk i at level j (j = K..1) and writes the K/V slot
   (i, j).  The clean slot (i, 0) exists only after a refresh node R(i), which
