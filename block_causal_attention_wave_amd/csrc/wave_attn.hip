@@ -337,8 +337,8 @@ struct TileFeed {
 // one workgroup per (work item, head, key split) over a contiguous range of
 // the node's key tiles.  Partial results are fp32 O normalised over the range
 // and its LSE, merged afterwards by wave_attn_combine_kernel.  In split-KV
-// mode, waves whose 32-row blocks hold no query row skip the arithmetic but
-// keep loading tiles.
+// mode and for work items shorter than a query tile, waves whose 32-row
+// blocks hold no query row skip the arithmetic but keep loading tiles.
 template <int HD, int W, int QB, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * W, 64 * W), amdgpu_waves_per_eu(W / 4, W / 4)))
 void wave_attn_kernel(AttnArgs a) {
@@ -378,276 +378,285 @@ void wave_attn_kernel(AttnArgs a) {
   const int32_t* ctx_g = a.ctx + 2 * nd[2];
   // first partial row of this item (split-KV: its round row)
   const int64_t prow0 = SPLIT ? (int64_t)q_offset + q_start : (int64_t)(item - a.num_direct) * kQTile;
-  const int lpad = a.lpad;
-  const int64_t slot_elems = (int64_t)a.heads * lpad * HD;
-  const __bf16* kcache = static_cast<const __bf16*>(a.k) + (int64_t)h * lpad * HD;
-  const __bf16* vcache = static_cast<const __bf16*>(a.vt) + (int64_t)h * HD * lpad;
 
-  // The gather list goes to LDS once, so that walking it inside the tile
-  // loop never waits on the vector-memory counter the K/V prefetch uses.
-  for (int e = threadIdx.x; e < 2 * ctx_count; e += C::THREADS) ctx_lds[e] = ctx_g[e];
-  // The V^T tile of ring stage NS-1 (where tile -1 would sit) starts as
-  // zeros: the first pipeline step multiplies it by a zero P.
-  for (int i = threadIdx.x; i < C::VBYTES / 16; i += C::THREADS)
-    reinterpret_cast<f32x4*>(lds + C::VBASE + (kStages - 1) * C::VBYTES)[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  __syncthreads();
-  int total_tiles = 0;
-  for (int e = 0; e < ctx_count; ++e) total_tiles += (ctx_lds[2 * e + 1] + kKT - 1) / kKT;
-  total_tiles = __builtin_amdgcn_readfirstlane(total_tiles);
-  int first_tile = 0;
-  if (partial) {
-    const int per = (total_tiles + nsplit - 1) / nsplit;
-    first_tile = min(total_tiles, split * per);
-    total_tiles = min(total_tiles, first_tile + per) - first_tile;
-    if (total_tiles <= 0) {  // empty range: weight zero in the merge
-      for (int r = threadIdx.x; r < q_rows; r += C::THREADS)
-        a.part_lse[((int64_t)split * a.heads + h) * a.part_rows + prow0 + r] = -INFINITY;
-      return;
+  // Two bodies: SKIP (split-KV, and work items shorter than a query tile)
+  // lets waves whose 32-row blocks hold no query row skip the arithmetic;
+  // full tiles run the body without that test.
+  auto run = [&](auto skip_tag) __attribute__((always_inline)) {
+    constexpr bool SKIP = decltype(skip_tag)::value;
+    const int lpad = a.lpad;
+    const int64_t slot_elems = (int64_t)a.heads * lpad * HD;
+    const __bf16* kcache = static_cast<const __bf16*>(a.k) + (int64_t)h * lpad * HD;
+    const __bf16* vcache = static_cast<const __bf16*>(a.vt) + (int64_t)h * HD * lpad;
+
+    // The gather list goes to LDS once, so that walking it inside the tile
+    // loop never waits on the vector-memory counter the K/V prefetch uses.
+    for (int e = threadIdx.x; e < 2 * ctx_count; e += C::THREADS) ctx_lds[e] = ctx_g[e];
+    // The V^T tile of ring stage NS-1 (where tile -1 would sit) starts as
+    // zeros: the first pipeline step multiplies it by a zero P.
+    for (int i = threadIdx.x; i < C::VBYTES / 16; i += C::THREADS)
+      reinterpret_cast<f32x4*>(lds + C::VBASE + (kStages - 1) * C::VBYTES)[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    __syncthreads();
+    int total_tiles = 0;
+    for (int e = 0; e < ctx_count; ++e) total_tiles += (ctx_lds[2 * e + 1] + kKT - 1) / kKT;
+    total_tiles = __builtin_amdgcn_readfirstlane(total_tiles);
+    int first_tile = 0;
+    if (partial) {
+      const int per = (total_tiles + nsplit - 1) / nsplit;
+      first_tile = min(total_tiles, split * per);
+      total_tiles = min(total_tiles, first_tile + per) - first_tile;
+      if (total_tiles <= 0) {  // empty range: weight zero in the merge
+        for (int r = threadIdx.x; r < q_rows; r += C::THREADS)
+          a.part_lse[((int64_t)split * a.heads + h) * a.part_rows + prow0 + r] = -INFINITY;
+        return;
+      }
     }
-  }
-  const bool active = !SPLIT || wv_u * QB * 32 < q_rows;  // wave-uniform (scalar compare)
+    const bool active = !SKIP || wv_u * QB * 32 < q_rows;  // wave-uniform (scalar compare)
 
-  // Q fragments (B operand of S^T): lane holds query (lane & 31) of block qb,
-  // dims 16c + 8*(lane>>5) .. +7.
-  const float c2 = a.scale_log2e;
-  bf16x8 qop[QB][C::NC];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int r = (wv * QB + qb) * 32 + (lane & 31);
-    const bool valid = r < q_rows;
-    const int64_t base = (int64_t)(q_offset + q_start + r) * a.q_row_stride + (int64_t)h * HD + 8 * (lane >> 5);
-#pragma unroll
-    for (int c = 0; c < C::NC; ++c) {
-      bf16x8 v;
-      if (!valid) {
-        for (int i = 0; i < 8; ++i) v[i] = (__bf16)0.0f;
-      } else if (a.q_fp32) {
-        const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(a.q) + base + 16 * c);
-        const f32x4 u = p[0], w = p[1];
-        for (int i = 0; i < 4; ++i) {
-          v[i] = (__bf16)u[i];
-          v[4 + i] = (__bf16)w[i];
+    // Q fragments (B operand of S^T): lane holds query (lane & 31) of block qb,
+    // dims 16c + 8*(lane>>5) .. +7.
+    const float c2 = a.scale_log2e;
+    bf16x8 qop[QB][C::NC];
+  #pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int r = (wv * QB + qb) * 32 + (lane & 31);
+      const bool valid = r < q_rows;
+      const int64_t base = (int64_t)(q_offset + q_start + r) * a.q_row_stride + (int64_t)h * HD + 8 * (lane >> 5);
+  #pragma unroll
+      for (int c = 0; c < C::NC; ++c) {
+        bf16x8 v;
+        if (!valid) {
+          for (int i = 0; i < 8; ++i) v[i] = (__bf16)0.0f;
+        } else if (a.q_fp32) {
+          const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(a.q) + base + 16 * c);
+          const f32x4 u = p[0], w = p[1];
+          for (int i = 0; i < 4; ++i) {
+            v[i] = (__bf16)u[i];
+            v[4 + i] = (__bf16)w[i];
+          }
+        } else {
+          v = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.q) + base + 16 * c);
         }
-      } else {
-        v = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.q) + base + 16 * c);
+        qop[qb][c] = v;
       }
-      qop[qb][c] = v;
     }
-  }
-  // Let the Q loads land here, on every path.  Their uses sit under
-  // wave-uniform branches the compiler cannot see through, and it would
-  // otherwise wait for every outstanding load (tile prefetches included)
-  // before the first MFMA of each pipeline step.
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int c = 0; c < C::NC; ++c) asm volatile("" ::"v"(qop[qb][c]));
-
-  f32x16 o[C::ND][QB];
-#pragma unroll
-  for (int db = 0; db < C::ND; ++db)
-#pragma unroll
+    // Let the Q loads land here, on every path.  Their uses sit under
+    // wave-uniform branches the compiler cannot see through, and it would
+    // otherwise wait for every outstanding load (tile prefetches included)
+    // before the first MFMA of each pipeline step.
+  #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[db][qb][i] = 0.0f;
-  // Softmax reference per query in log2 units (c2 * a raw score): exact row
-  // max of the first block, raised lazily afterwards.
-  float mref[QB], l[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) l[qb] = 0.0f;
+  #pragma unroll
+      for (int c = 0; c < C::NC; ++c) asm volatile("" ::"v"(qop[qb][c]));
 
-  TileFeed<HD> ld(ctx_lds, ctx_count, reinterpret_cast<const char*>(kcache),
-                  reinterpret_cast<const char*>(vcache), slot_elems * 2, first_tile);
-  const TileOffsets<HD, W, QB> toff(lpad, wv, lane);
-  auto issue = [&](int stage) {
-    issue_tile<HD, W, QB>(lds + stage * C::KBYTES, ld.kt, ld.vt, toff, wv_u);
-    ld.next();
-  };
-  constexpr int kWaitExp = (0x7 << 4) | (0xF << 8);
-  auto wait_tiles = [&](int later) {  // wait until at most `later` tiles of loads are in flight
-    if (later >= 2) __builtin_amdgcn_s_waitcnt(kWaitExp | ((2 * C::LOADS) & 15) | (((2 * C::LOADS) >> 4) << 14));
-    else if (later == 1) __builtin_amdgcn_s_waitcnt(kWaitExp | (C::LOADS & 15) | ((C::LOADS >> 4) << 14));
-    else __builtin_amdgcn_s_waitcnt(kWaitExp);
-  };
-  // Raw barrier: the wait above covers this thread's LDS fills, and the
-  // compiler barriers keep LDS reads on their side of it.
-  auto barrier = [&]() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
+    f32x16 o[C::ND][QB];
+  #pragma unroll
+    for (int db = 0; db < C::ND; ++db)
+  #pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+  #pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][qb][i] = 0.0f;
+    // Softmax reference per query in log2 units (c2 * a raw score): exact row
+    // max of the first block, raised lazily afterwards.
+    float mref[QB], l[QB];
+  #pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l[qb] = 0.0f;
 
-  // Prologue: tiles 0..NS-2 in flight; scores of block 0 with an exact row max.
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < total_tiles) issue(s);
-  wait_tiles(min(total_tiles - 1, NS - 2));
-  barrier();
-  Walker cur(ctx_lds, ctx_count);
-  cur.skip(first_tile);
-  f32x16 sa[QB], sb[QB];
-  if (active) {
-    qk_block<HD, QB>(lds, 0, qop, sa, lane);
-    if (cur.valid() < 32) mask_block<QB>(sa, cur.valid(), lane);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) mref[qb] = c2 * block_rowmax(sa[qb]);
-  }
+    TileFeed<HD> ld(ctx_lds, ctx_count, reinterpret_cast<const char*>(kcache),
+                    reinterpret_cast<const char*>(vcache), slot_elems * 2, first_tile);
+    const TileOffsets<HD, W, QB> toff(lpad, wv, lane);
+    auto issue = [&](int stage) {
+      issue_tile<HD, W, QB>(lds + stage * C::KBYTES, ld.kt, ld.vt, toff, wv_u);
+      ld.next();
+    };
+    constexpr int kWaitExp = (0x7 << 4) | (0xF << 8);
+    auto wait_tiles = [&](int later) {  // wait until at most `later` tiles of loads are in flight
+      if (later >= 2) __builtin_amdgcn_s_waitcnt(kWaitExp | ((2 * C::LOADS) & 15) | (((2 * C::LOADS) >> 4) << 14));
+      else if (later == 1) __builtin_amdgcn_s_waitcnt(kWaitExp | (C::LOADS & 15) | ((C::LOADS >> 4) << 14));
+      else __builtin_amdgcn_s_waitcnt(kWaitExp);
+    };
+    // Raw barrier: the wait above covers this thread's LDS fills, and the
+    // compiler barriers keep LDS reads on their side of it.
+    auto barrier = [&]() {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
 
-  // A block's probabilities were formed against the current reference; if
-  // some lane's sum over its 16 keys exceeds 2^kRescaleLog2 (a score above the
-  // reference by more than that, or an overflow to inf), the block is redone:
-  // its scores are recomputed from the K tile still in LDS, the reference is
-  // raised to the block's exact row max (rescaling O and l), and the
-  // probabilities are formed again.  Rare after the first block, which sets the
-  // reference exactly; otherwise the block's sums go straight into l.
-  auto settle = [&](float (&bsum)[QB], bf16x8 (&pop)[QB][2], const char* kst, int kb, int valid)
-      __attribute__((always_inline)) {
-    bool big = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) big |= bsum[qb] > kRescaleSum;
-    if (__builtin_amdgcn_ballot_w64(big) != 0) {
-      f32x16 sr[QB];
-      qk_block<HD, QB>(kst, kb, qop, sr, lane);
-      if (valid < 32) mask_block<QB>(sr, valid, lane);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float delta = fmaxf(c2 * block_rowmax(sr[qb]) - mref[qb], 0.0f);
-        const float alpha = __builtin_amdgcn_exp2f(-delta);
-        mref[qb] += delta;
-        l[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::ND; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[db][qb][i] *= alpha;
-      }
-      softmax_block<QB>(sr, c2, mref, pop, bsum);
-    }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) l[qb] += bsum[qb];
-  };
-
-  // Software pipeline over 32-key blocks: step j issues the scores of block
-  // j+1 and the P.V product of block j-1 on the matrix cores, then forms the
-  // probabilities of block j on the vector ALUs; the three are independent,
-  // so one wave's MFMA and VALU work overlap.  Block j's P waits in
-  // registers (pprev) until step j+1.  Each 64-key tile is two steps (block 0
-  // with scores in sa, block 1 with scores in sb); the ring stage of tile n is
-  // n % NS and the loop is unrolled NS tiles so that every LDS operand address
-  // is a per-lane base plus an immediate.
-  // The V^T region starts at 64 KiB, past the reach of an LDS instruction's
-  // immediate offset; hiding its start from the compiler makes it part of the
-  // per-lane base register, so the stage and block offsets stay immediates.
-  uint32_t vregion = C::VBASE;
-  asm volatile("" : "+s"(vregion));
-  bf16x8 pprev[QB][2];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pprev[qb][hh][i] = (__bf16)0.0f;
-  auto step = [&](int n, auto stage_tag, auto kb_tag, f32x16 (&scur)[QB], f32x16 (&snext)[QB])
-      __attribute__((always_inline)) {
-    constexpr int ST = decltype(stage_tag)::value;
-    constexpr int KB = decltype(kb_tag)::value;
-    constexpr int SP = (ST + NS - 1) % NS;  // stage of tile n-1
-    const char* kst = lds + ST * C::KBYTES;
-    const char* vst = lds + vregion + ST * C::VBYTES;
-    const int valid = cur.valid();
-    const bool has_next = KB == 0 || n + 1 < total_tiles;
-    if constexpr (KB == 1) {
-      wait_tiles(min(total_tiles - 2 - n, NS - 3));
-      barrier();
-      if (n + NS - 1 < total_tiles) issue((ST + NS - 1) % NS);
-    }
+    // Prologue: tiles 0..NS-2 in flight; scores of block 0 with an exact row max.
+    for (int s = 0; s < NS - 1; ++s)
+      if (s < total_tiles) issue(s);
+    wait_tiles(min(total_tiles - 1, NS - 2));
+    barrier();
+    Walker cur(ctx_lds, ctx_count);
+    cur.skip(first_tile);
+    f32x16 sa[QB], sb[QB];
     if (active) {
-      // Without a next block the scores are formed from a stale stage and
-      // never used; for the first block of the walk, pprev and the V^T half
-      // it meets are zero.
-      qk_block<HD, QB>(lds + (KB == 0 ? ST : (ST + 1) % NS) * C::KBYTES, KB ^ 1, qop, snext, lane);
+      qk_block<HD, QB>(lds, 0, qop, sa, lane);
+      if (cur.valid() < 32) mask_block<QB>(sa, cur.valid(), lane);
+  #pragma unroll
+      for (int qb = 0; qb < QB; ++qb) mref[qb] = c2 * block_rowmax(sa[qb]);
+    }
+
+    // A block's probabilities were formed against the current reference; if
+    // some lane's sum over its 16 keys exceeds 2^kRescaleLog2 (a score above the
+    // reference by more than that, or an overflow to inf), the block is redone:
+    // its scores are recomputed from the K tile still in LDS, the reference is
+    // raised to the block's exact row max (rescaling O and l), and the
+    // probabilities are formed again.  Rare after the first block, which sets the
+    // reference exactly; otherwise the block's sums go straight into l.
+    auto settle = [&](float (&bsum)[QB], bf16x8 (&pop)[QB][2], const char* kst, int kb, int valid)
+        __attribute__((always_inline)) {
+      bool big = false;
+  #pragma unroll
+      for (int qb = 0; qb < QB; ++qb) big |= bsum[qb] > kRescaleSum;
+      if (__builtin_amdgcn_ballot_w64(big) != 0) {
+        f32x16 sr[QB];
+        qk_block<HD, QB>(kst, kb, qop, sr, lane);
+        if (valid < 32) mask_block<QB>(sr, valid, lane);
+  #pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float delta = fmaxf(c2 * block_rowmax(sr[qb]) - mref[qb], 0.0f);
+          const float alpha = __builtin_amdgcn_exp2f(-delta);
+          mref[qb] += delta;
+          l[qb] *= alpha;
+  #pragma unroll
+          for (int db = 0; db < C::ND; ++db)
+  #pragma unroll
+            for (int i = 0; i < 16; ++i) o[db][qb][i] *= alpha;
+        }
+        softmax_block<QB>(sr, c2, mref, pop, bsum);
+      }
+  #pragma unroll
+      for (int qb = 0; qb < QB; ++qb) l[qb] += bsum[qb];
+    };
+
+    // Software pipeline over 32-key blocks: step j issues the scores of block
+    // j+1 and the P.V product of block j-1 on the matrix cores, then forms the
+    // probabilities of block j on the vector ALUs; the three are independent,
+    // so one wave's MFMA and VALU work overlap.  Block j's P waits in
+    // registers (pprev) until step j+1.  Each 64-key tile is two steps (block 0
+    // with scores in sa, block 1 with scores in sb); the ring stage of tile n is
+    // n % NS and the loop is unrolled NS tiles so that every LDS operand address
+    // is a per-lane base plus an immediate.
+    // The V^T region starts at 64 KiB, past the reach of an LDS instruction's
+    // immediate offset; hiding its start from the compiler makes it part of the
+    // per-lane base register, so the stage and block offsets stay immediates.
+    uint32_t vregion = C::VBASE;
+    asm volatile("" : "+s"(vregion));
+    bf16x8 pprev[QB][2];
+  #pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+  #pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) pprev[qb][hh][i] = (__bf16)0.0f;
+    auto step = [&](int n, auto stage_tag, auto kb_tag, f32x16 (&scur)[QB], f32x16 (&snext)[QB])
+        __attribute__((always_inline)) {
+      constexpr int ST = decltype(stage_tag)::value;
+      constexpr int KB = decltype(kb_tag)::value;
+      constexpr int SP = (ST + NS - 1) % NS;  // stage of tile n-1
+      const char* kst = lds + ST * C::KBYTES;
+      const char* vst = lds + vregion + ST * C::VBYTES;
+      const int valid = cur.valid();
+      const bool has_next = KB == 0 || n + 1 < total_tiles;
+      if constexpr (KB == 1) {
+        wait_tiles(min(total_tiles - 2 - n, NS - 3));
+        barrier();
+        if (n + NS - 1 < total_tiles) issue((ST + NS - 1) % NS);
+      }
+      if (active) {
+        // Without a next block the scores are formed from a stale stage and
+        // never used; for the first block of the walk, pprev and the V^T half
+        // it meets are zero.
+        qk_block<HD, QB>(lds + (KB == 0 ? ST : (ST + 1) % NS) * C::KBYTES, KB ^ 1, qop, snext, lane);
+        if constexpr (KB == 0) {
+          pv_block<HD, QB>(lds + vregion + SP * C::VBYTES, 1, pprev, o, lane);
+        } else {
+          pv_block<HD, QB>(vst, 0, pprev, o, lane);
+        }
+        float bsum[QB];
+        softmax_block<QB>(scur, c2, mref, pprev, bsum);
+        // Instruction order of the step: two LDS operand reads ahead, then
+        // (MFMA, 3 VALU, LDS read) groups.
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  #pragma unroll
+        for (int i = 0; i < 16 - 2; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+  #pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+        settle(bsum, pprev, kst, KB, valid - 32 * KB);
+      }
       if constexpr (KB == 0) {
-        pv_block<HD, QB>(lds + vregion + SP * C::VBYTES, 1, pprev, o, lane);
+        if (active && valid < 64) mask_block<QB>(snext, valid - 32, lane);
       } else {
-        pv_block<HD, QB>(vst, 0, pprev, o, lane);
+        cur.next();
+        if (has_next && active && cur.valid() < 32) mask_block<QB>(snext, cur.valid(), lane);
       }
-      float bsum[QB];
-      softmax_block<QB>(scur, c2, mref, pprev, bsum);
-      // Instruction order of the step: two LDS operand reads ahead, then
-      // (MFMA, 3 VALU, LDS read) groups.
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-      for (int i = 0; i < 16 - 2; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-      }
-      settle(bsum, pprev, kst, KB, valid - 32 * KB);
+    };
+    auto tile = [&](int n, auto stage_tag) __attribute__((always_inline)) {
+      step(n, stage_tag, std::integral_constant<int, 0>{}, sa, sb);
+      step(n, stage_tag, std::integral_constant<int, 1>{}, sb, sa);
+    };
+
+    static_assert(NS == 4, "the tile loop below is unrolled for a 4-stage ring");
+    for (int n = 0; n < total_tiles; n += NS) {
+      tile(n, std::integral_constant<int, 0>{});
+      if (n + 1 < total_tiles) tile(n + 1, std::integral_constant<int, 1>{});
+      if (n + 2 < total_tiles) tile(n + 2, std::integral_constant<int, 2>{});
+      if (n + 3 < total_tiles) tile(n + 3, std::integral_constant<int, 3>{});
     }
-    if constexpr (KB == 0) {
-      if (active && valid < 64) mask_block<QB>(snext, valid - 32, lane);
-    } else {
-      cur.next();
-      if (has_next && active && cur.valid() < 32) mask_block<QB>(snext, cur.valid(), lane);
+    // P.V of the last block (block 1 of the last tile).
+    if (active) pv_block<HD, QB>(lds + vregion + ((total_tiles - 1) % NS) * C::VBYTES, 1, pprev, o, lane);
+
+    // Epilogue: O = O^T / l, LSE = ln2 * (mref + log2 l).
+    if (!active) return;
+    const int64_t orow_stride = (int64_t)a.heads * HD;
+  #pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float ltot = halfwave_sum(l[qb]);
+      const float inv = 1.0f / ltot;
+      const float lse = (mref[qb] + __log2f(ltot)) * 0.69314718055994531f;
+      const int r = (wv * QB + qb) * 32 + (lane & 31);
+      if (r < q_rows) {
+        const int64_t grow = q_offset + q_start + r;
+        if (partial) {
+          const int64_t prow = prow0 + r;
+          float* orow = a.part_o + (((int64_t)split * a.part_rows + prow) * a.heads + h) * HD;
+  #pragma unroll
+          for (int db = 0; db < C::ND; ++db)
+  #pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              f32x4 v;
+  #pragma unroll
+              for (int i = 0; i < 4; ++i) v[i] = o[db][qb][4 * g + i] * inv;
+              *reinterpret_cast<f32x4*>(orow + db * 32 + g * 8 + (lane >> 5) * 4) = v;
+            }
+          if (lane < 32) a.part_lse[((int64_t)split * a.heads + h) * a.part_rows + prow] = lse;
+        } else {
+          __bf16* orow = static_cast<__bf16*>(a.o) + grow * orow_stride + (int64_t)h * HD;
+  #pragma unroll
+          for (int db = 0; db < C::ND; ++db)
+  #pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              bf16x4 v;
+  #pragma unroll
+              for (int i = 0; i < 4; ++i) v[i] = (__bf16)(o[db][qb][4 * g + i] * inv);
+              *reinterpret_cast<bf16x4*>(orow + db * 32 + g * 8 + (lane >> 5) * 4) = v;
+            }
+          if (a.lse != nullptr && lane < 32) a.lse[(int64_t)h * a.lse_stride + grow] = lse;
+        }
+      }
     }
   };
-  auto tile = [&](int n, auto stage_tag) __attribute__((always_inline)) {
-    step(n, stage_tag, std::integral_constant<int, 0>{}, sa, sb);
-    step(n, stage_tag, std::integral_constant<int, 1>{}, sb, sa);
-  };
-
-  static_assert(NS == 4, "the tile loop below is unrolled for a 4-stage ring");
-  for (int n = 0; n < total_tiles; n += NS) {
-    tile(n, std::integral_constant<int, 0>{});
-    if (n + 1 < total_tiles) tile(n + 1, std::integral_constant<int, 1>{});
-    if (n + 2 < total_tiles) tile(n + 2, std::integral_constant<int, 2>{});
-    if (n + 3 < total_tiles) tile(n + 3, std::integral_constant<int, 3>{});
-  }
-  // P.V of the last block (block 1 of the last tile).
-  if (active) pv_block<HD, QB>(lds + vregion + ((total_tiles - 1) % NS) * C::VBYTES, 1, pprev, o, lane);
-
-  // Epilogue: O = O^T / l, LSE = ln2 * (mref + log2 l).
-  if (!active) return;
-  const int64_t orow_stride = (int64_t)a.heads * HD;
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float ltot = halfwave_sum(l[qb]);
-    const float inv = 1.0f / ltot;
-    const float lse = (mref[qb] + __log2f(ltot)) * 0.69314718055994531f;
-    const int r = (wv * QB + qb) * 32 + (lane & 31);
-    if (r < q_rows) {
-      const int64_t grow = q_offset + q_start + r;
-      if (partial) {
-        const int64_t prow = prow0 + r;
-        float* orow = a.part_o + (((int64_t)split * a.part_rows + prow) * a.heads + h) * HD;
-#pragma unroll
-        for (int db = 0; db < C::ND; ++db)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            f32x4 v;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = o[db][qb][4 * g + i] * inv;
-            *reinterpret_cast<f32x4*>(orow + db * 32 + g * 8 + (lane >> 5) * 4) = v;
-          }
-        if (lane < 32) a.part_lse[((int64_t)split * a.heads + h) * a.part_rows + prow] = lse;
-      } else {
-        __bf16* orow = static_cast<__bf16*>(a.o) + grow * orow_stride + (int64_t)h * HD;
-#pragma unroll
-        for (int db = 0; db < C::ND; ++db)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            bf16x4 v;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = (__bf16)(o[db][qb][4 * g + i] * inv);
-            *reinterpret_cast<bf16x4*>(orow + db * 32 + g * 8 + (lane >> 5) * 4) = v;
-          }
-        if (a.lse != nullptr && lane < 32) a.lse[(int64_t)h * a.lse_stride + grow] = lse;
-      }
-    }
-  }
+  if (SPLIT || q_rows < kQTile) run(std::true_type{});
+  else run(std::false_type{});
 }
 
 // Merge of partial results (one thread per partial row, head and 8 output
