@@ -176,8 +176,8 @@ int32_t device_cus() {
   return cus;
 }
 
-// Splits for split-KV attention: the count whose simulated dispatch onto the
-// current device's compute units finishes first (merge included), 1..64.
+// Splits for split-KV attention: the most whose workgroups fit the current
+// device's compute units in one dispatch wave, 1..64.
 int32_t auto_splits(const wave::Plan& p, int32_t round, int32_t heads, int32_t head_dim) {
   return wave::choose_splits(p, round, heads, head_dim, device_cus());
 }

@@ -62,23 +62,19 @@ double simulate_round(const Plan& p, int32_t round, int32_t heads, int32_t cus, 
 }
 
 int32_t choose_splits(const Plan& p, int32_t round, int32_t heads, int32_t head_dim, int32_t cus) {
+  (void)head_dim;
   const std::vector<int64_t> tiles = item_tiles(p, round);
-  const int32_t n = static_cast<int32_t>(tiles.size());
+  const int64_t n = static_cast<int64_t>(tiles.size());
   if (n == 0 || heads < 1 || cus < 1) return 1;
-  const double tile_s = kTileSeconds * head_dim / 128.0;
-  const double rows = static_cast<double>(p.round_q_rows[round]);
-  int32_t best = 1;
-  double best_t = 0.0;
-  for (int32_t s = 1; s <= 64; ++s) {
-    const TailSplit t{n, s};
-    double v = simulate(tiles, heads, cus, t);
-    if (s > 1) v += (static_cast<double>(s) * rows * heads * head_dim * 4.0 / kMergeBytesPerSecond + kLaunchSeconds) / tile_s;
-    if (s == 1 || v < best_t) {
-      best_t = v;
-      best = s;
-    }
-  }
-  return best;
+  // Split-KV items are short query blocks: a workgroup does little arithmetic
+  // per key tile and streams its range from HBM, so the round costs its bytes
+  // at the chip's streaming rate, plus one workgroup start-up (gather list,
+  // then the first tile's latency) per dispatch wave, plus the merge.  A
+  // second wave pays that start-up again and a partly filled one leaves units
+  // idle, so the count that fills the compute units exactly once wins.
+  const int64_t longest = *std::max_element(tiles.begin(), tiles.end());
+  const int64_t s = std::min<int64_t>({static_cast<int64_t>(cus) / (n * heads), longest, 64});
+  return static_cast<int32_t>(std::max<int64_t>(s, 1));
 }
 
 TailSplit choose_tail_split(const Plan& p, int32_t round, int32_t heads, int32_t head_dim, int32_t cus) {

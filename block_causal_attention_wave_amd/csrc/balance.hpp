@@ -25,8 +25,9 @@ struct TailSplit {
 TailSplit choose_tail_split(const Plan& p, int32_t round, int32_t heads, int32_t head_dim, int32_t cus);
 
 // Key splits for split-KV attention of `round` (every work item cut into
-// that many ranges), 1..64: the count with the shortest simulated round,
-// merge pass included.
+// that many ranges), 1..64: the most that still fit the round's workgroups
+// (items x heads x splits) onto the `cus` compute units in one dispatch wave,
+// at most the longest item's key-tile count.
 int32_t choose_splits(const Plan& p, int32_t round, int32_t heads, int32_t head_dim, int32_t cus);
 
 // Simulated duration, in key-tile times, of the round with that split: each

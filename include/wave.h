@@ -218,7 +218,9 @@ int32_t wave_attn(const wave_plan_t* plan, const void* d_desc, int32_t round,
  * LSE = log sum_k exp(LSE_k), O = sum_k exp(LSE_k - LSE) O_k.  Results equal
  * wave_attn's up to rounding (the reduction order differs).
  *   num_splits: >= 1, or 0 to let the library choose from the round's work
- *               and the current device's compute-unit count.
+ *               and the current device's compute-unit count: the most splits
+ *               whose workgroups (work items x heads x splits) fill the units
+ *               in one dispatch wave, 1..64.
  *   workspace : device memory of at least wave_attn_splitkv_workspace()
  *               bytes, 256-byte aligned, owned by the caller; its contents
  *               need no initialisation and are scratch after the call.

@@ -256,6 +256,26 @@ def test_tail_balancing_choice_and_workspace_checks():
     assert attn(C.c_void_p(0x10010), 1 << 40) == _lib.WAVE_ERR_INVALID_ARG
 
 
+def test_splitkv_auto_split_count_fills_one_dispatch_wave():
+    """num_splits = 0: the most splits whose workgroups (items x heads x splits)
+    fit 256 compute units in one dispatch wave (the device count falls back to
+    256 without a GPU), at most the longest item's key-tile count."""
+    lib = _lib.load()
+    w = WORKLOADS[6]
+    pn = native(w.B, w.K, op.SAME_LEVEL, op.WAVE, w.history_cap, w.chunk_len, w.cond_len, query_len=w.query_len)
+    items = int(pn.round_work_begin[w.round + 1] - pn.round_work_begin[w.round])
+    b, s = C.c_size_t(), C.c_int32()
+    assert lib.wave_attn_splitkv_workspace(pn.handle, w.round, w.heads, w.head_dim, 0, C.byref(b), C.byref(s)) == 0
+    assert items == 2 and s.value == 256 // (items * w.heads) == 3
+    # few key tiles: capped at the longest item's tile count
+    small = native(2, 1, op.PROGRESSIVE, op.WAVE, -1, 100, 0, query_len=8)
+    assert lib.wave_attn_splitkv_workspace(small.handle, 1, 1, 64, 0, C.byref(b), C.byref(s)) == 0
+    assert s.value == 4  # round 1: R(0) and U(1,1); U(1,1) reads 2 slots of 2 key tiles
+    # more workgroups than units: one split
+    assert lib.wave_attn_splitkv_workspace(pn.handle, w.round, 200, w.head_dim, 0, C.byref(b), C.byref(s)) == 0
+    assert s.value == 1
+
+
 def test_chain_calls_validate_before_launch():
     """qkv_project / chain_store reject bad arguments on the host (no GPU needed)."""
     lib = _lib.load()
