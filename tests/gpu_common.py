@@ -59,6 +59,29 @@ class HostInputs:
         return round_to_bf16(k).astype(np.float64), round_to_bf16(v).astype(np.float64)
 
 
+def freed_after(plan):
+    """{round t: physical slots whose occupant (the logical slot last written
+    there) no round after t reads}: the slots a rolling cache may reuse."""
+    last = {}
+    for t in range(plan.num_rounds):
+        for n in plan.round_nodes(t).tolist():
+            for (c, lv, _p, _l) in plan.node_ctx(n).tolist():
+                last[(c, lv)] = t
+    occupant, out = {}, {}
+    for t in range(plan.num_rounds):
+        for (c, lv, p, _l) in plan.round_writes(t).tolist():
+            occupant[p] = (c, lv)
+        out[t] = sorted(p for p, key in occupant.items() if last.get(key, -1) <= t)
+    return out
+
+
+def poison_slots(cache, slots):
+    """NaN-fill whole physical slots of a cache (K and V^T)."""
+    for p in slots:
+        cache.k[p].fill_(float("nan"))
+        cache.vt[p].fill_(float("nan"))
+
+
 def gpu_rollout(plan, inputs, device, scale, src_dtype="fp32", poison=True, perturb=None, splits=None,
                 balance=True):
     """Run every round of `plan` on the GPU; return {(chunk, level): (O fp32 [L,h,d], LSE [h,L])}.
@@ -66,6 +89,9 @@ def gpu_rollout(plan, inputs, device, scale, src_dtype="fp32", poison=True, pert
     perturb(chunk, level, k, v) -> (k, v) may alter the fresh K/V of a slot.
     splits: None = wave_attn, else wave_attn_splitkv with that many splits (0 = auto).
     balance: wave_attn's tail balancing (library's choice for this device).
+    poison: the cache starts as NaN, and after every round each slot whose
+    occupant no later round reads is NaN-filled again, so a read of a freed
+    slot shows up as a non-finite output.
     """
     import torch
     dt = torch.float32 if src_dtype == "fp32" else torch.bfloat16
@@ -73,6 +99,7 @@ def gpu_rollout(plan, inputs, device, scale, src_dtype="fp32", poison=True, pert
     cache = wv.KVCache(plan.num_phys_slots, inputs.heads, inputs.hd, plan.lpad(), device,
                        fill=float("nan") if poison else 0.0)
     outs = {}
+    freed = freed_after(plan) if poison else {}
     for t in range(plan.num_rounds):
         ks, vs = [], []
         for (c, lv, _pid, _ln) in plan.round_writes(t).tolist():
@@ -96,6 +123,7 @@ def gpu_rollout(plan, inputs, device, scale, src_dtype="fp32", poison=True, pert
         for n in nodes:
             a, b = n[4], n[4] + n[5]
             outs[(n[0], n[1])] = (o[a:b], lse[:, a:b])
+        poison_slots(cache, freed.get(t, []))
     return outs
 
 

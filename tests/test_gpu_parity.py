@@ -11,8 +11,8 @@ import block_causal_attention_wave_amd as wv
 from oracle import plan as op
 from oracle.attention import round_to_bf16
 import wave_inputs as wi
-from gpu_common import (HostInputs, LSE_ABS, MAX_ABS, MEAN_ABS, compare, gpu_rollout, log, oracle_rollout,
-                        sample_rows)
+from gpu_common import (HostInputs, LSE_ABS, MAX_ABS, MEAN_ABS, compare, freed_after, gpu_rollout, log,
+                        oracle_rollout, poison_slots, sample_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -151,11 +151,14 @@ def _device_round(w, policy, layer, t_meas, device, rows_per_node=256, heads=Non
                                   wi.device_tensor(w, layer, c, lv, "v", device, policy))
         return dev_cache[(c, lv)]
 
+    freed = freed_after(plan)
     for t in range(t_meas + 1):
         ws = plan.round_writes(t).tolist()
         k_src = torch.cat([kv_dev(c, lv)[0] for (c, lv, _, _) in ws])
         v_src = torch.cat([kv_dev(c, lv)[1] for (c, lv, _, _) in ws])
         wv.kv_write(plan, desc, t, cache, k_src, v_src)
+        if t < t_meas:  # the rolling cache: slots no later round reads are poisoned
+            poison_slots(cache, freed[t])
     nodes = plan.round_nodes(t_meas).tolist()
     qs = {(n[0], n[1]): wi.device_tensor(w, layer, n[0], n[1], "q", device, policy) for n in nodes}
     q = torch.cat([qs[(n[0], n[1])] for n in nodes])

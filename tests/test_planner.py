@@ -256,6 +256,27 @@ def test_tail_balancing_choice_and_workspace_checks():
     assert attn(C.c_void_p(0x10010), 1 << 40) == _lib.WAVE_ERR_INVALID_ARG
 
 
+def test_poisoned_slots_are_rewritten_before_any_later_read():
+    """The GPU tests NaN-fill, after each round, the physical slots whose
+    occupant no later round reads.  Over the capped-history long-video plan
+    (B=28, K=4, H=6) such a slot is read again only after a rewrite, and the
+    rolling cache does reuse slots."""
+    from gpu_common import freed_after
+    pn = native(28, 4, op.PROGRESSIVE, op.WAVE, 6, 16)
+    freed = freed_after(pn)
+    written = {t: {w[2] for w in pn.round_writes(t).tolist()} for t in range(pn.num_rounds)}
+    reused = 0
+    for t, slots in freed.items():
+        for p in slots:
+            for u in range(t + 1, pn.num_rounds):
+                if p in written[u]:
+                    reused += 1
+                    break
+                read = {e[2] for n in pn.round_nodes(u).tolist() for e in pn.node_ctx(n).tolist()}
+                assert p not in read, (t, p, u)
+    assert reused > 0 and pn.num_phys_slots < len(pn.writes)
+
+
 def test_splitkv_auto_split_count_fills_one_dispatch_wave():
     """num_splits = 0: the most splits whose workgroups (items x heads x splits)
     fit 256 compute units in one dispatch wave (the device count falls back to
