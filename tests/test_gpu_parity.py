@@ -224,6 +224,62 @@ def test_long_video_capped_history_sampled(gpu_device):
         log(f"  node {key}: {s}")
 
 
+@pytest.mark.parametrize("layer", [0, 14, 29])
+@pytest.mark.parametrize("policy", [wi.CLEAN, wi.SAME_LEVEL, wi.PROGRESSIVE])
+def test_wan13b_k5_rollout_sampled(gpu_device, policy, layer):
+    """The 832x480 seven-chunk K=5 rollouts at full size (one of the 30
+    layers): every round of the pipelined plan on the GPU, with freed slots
+    poisoned, against the oracle's serial rollout on sampled rows of 2 heads,
+    for every node of chunks 0, 3 and 6."""
+    import torch
+    w = wi.WORKLOADS[3]
+    heads = [0, 7]
+    log(f"{w.name}: policy {policy} layer {layer}, all rounds")
+    plan = wv.wave_plan(B=w.B, K=w.K, policy=policy, sched=wv.WAVE, chunk_len=w.chunk_len)
+    desc = plan.upload(gpu_device)
+    cache = wv.KVCache(plan.num_phys_slots, w.heads, w.head_dim, plan.lpad(), gpu_device, fill=float("nan"))
+    freed = freed_after(plan)
+    rows = sample_rows(w.chunk_len, 96)
+    want = {(n[0], n[1]) for n in plan.nodes.tolist() if n[0] in (0, 3, 6)}
+    host = {}
+
+    def dev(c, lv, kind):
+        t = wi.device_tensor(w, layer, c, lv, kind, gpu_device, policy)
+        host[(c, lv, kind)] = t[:, heads].float().cpu().numpy().astype(np.float64)
+        return t
+
+    got = {}
+    for t in range(plan.num_rounds):
+        ws = plan.round_writes(t).tolist()
+        k_src = torch.cat([dev(c, lv, "k") for (c, lv, _, _) in ws])
+        v_src = torch.cat([dev(c, lv, "v") for (c, lv, _, _) in ws])
+        wv.kv_write(plan, desc, t, cache, k_src, v_src)
+        nodes = plan.round_nodes(t).tolist()
+        q = torch.cat([dev(n[0], n[1], "q") for n in nodes])
+        o, lse = wv.wave_attn(plan, desc, t, cache, q, w.scale)
+        torch.cuda.synchronize()
+        for n in nodes:
+            if (n[0], n[1]) in want:
+                sel = n[4] + rows
+                got[(n[0], n[1])] = (o[sel][:, heads].float().cpu().numpy(), lse[heads][:, sel].cpu().numpy())
+        del k_src, v_src, q, o, lse
+        poison_slots(cache, freed[t])
+
+    class DevInputs:
+        def q64(self, c, lv):
+            return host[(c, lv, "q")]
+
+        def kv64(self, c, lv):
+            return host[(c, lv, "k")], host[(c, lv, "v")]
+
+    ref = oracle_rollout(w.B, w.K, policy, -1, w.chunk_len, 0, DevInputs(), w.scale, rows=lambda c, lv: rows,
+                         want=want)
+    assert set(ref) == want == set(got)
+    for key in sorted(want):
+        s = compare(got[key][0], got[key][1], ref[key][0], ref[key][1], f"node {key}")
+    log(f"  {len(want)} nodes; last {s}")
+
+
 SPLIT_GRID = [
     # policy, H, cond, L, query_len, heads, hd, splits
     (wi.PROGRESSIVE, -1, 0, 300, 0, 2, 128, 3),
