@@ -27,8 +27,8 @@ from ._lib import (WAVE_CLEAN, WAVE_DTYPE_BF16, WAVE_DTYPE_FP32, WAVE_KEY_TILE, 
 CLEAN, SAME_LEVEL, PROGRESSIVE = WAVE_CLEAN, WAVE_SAME_LEVEL, WAVE_PROGRESSIVE
 SERIAL, WAVE = WAVE_SCHED_SERIAL, WAVE_SCHED_WAVE
 
-__all__ = ["Plan", "KVCache", "wave_plan", "kv_write", "wave_attn", "wave_attn_splitkv",
-           "splitkv_workspace_bytes", "WaveError",
+__all__ = ["Plan", "KVCache", "wave_plan", "kv_write", "wave_attn", "wave_round", "wave_attn_splitkv",
+           "attn_workspace", "splitkv_workspace_bytes", "qkv_project", "chain_store", "WaveError",
            "CLEAN", "SAME_LEVEL", "PROGRESSIVE", "SERIAL", "WAVE", "WAVE_LEVEL_COND",
            "WAVE_Q_TILE", "WAVE_KEY_TILE", "WAVE_NODE_UPDATE", "WAVE_NODE_REFRESH"]
 
@@ -219,6 +219,54 @@ def wave_attn(plan: Plan, d_desc, round: int, cache: KVCache, q, scale: float, o
                                      C.c_void_p(lse.data_ptr() if lse is not None else 0),
                                      float(scale), C.c_void_p(ws_ptr), ws_bytes, _stream_ptr(stream)))
     return o, lse
+
+
+def wave_round(plan: Plan, d_desc, round: int, caches, k_srcs, v_srcs, qs, scale: float, os=None, lses=None,
+               want_lse=True, stream=None, balance=True, workspace=None):
+    """One round of every layer in one call: for each layer, kv_write of its
+    fresh K/V into caches[l], then wave_attn of qs[l], all enqueued on one
+    stream with no host synchronisation.  k_srcs / v_srcs share a dtype and row
+    stride, as do the qs.  Returns (os, lses), one entry per layer; the layers
+    share one tail-balancing workspace (allocated here when not given)."""
+    import torch
+    n = len(caches)
+    if n < 1 or not (len(k_srcs) == len(v_srcs) == len(qs) == n):
+        raise ValueError("caches, k_srcs, v_srcs and qs need one entry per layer")
+    if os is not None and len(os) != n or lses is not None and len(lses) != n:
+        raise ValueError("os and lses need one entry per layer")
+    rows = int(plan.round_src_rows[round]) if 0 <= round < plan.num_rounds else 0
+    outs_o, outs_l = [], []
+    for l in range(n):
+        _check_rows(k_srcs[l], rows, caches[l].heads, caches[l].head_dim, f"k_srcs[{l}]")
+        _check_rows(v_srcs[l], rows, caches[l].heads, caches[l].head_dim, f"v_srcs[{l}]")
+        o, lse = _attn_outputs(plan, round, caches[l], qs[l], None if os is None else os[l],
+                               None if lses is None else lses[l], want_lse)
+        outs_o.append(o)
+        outs_l.append(lse)
+    for t in list(k_srcs) + list(v_srcs):
+        if t.dtype != k_srcs[0].dtype or t.stride(0) != k_srcs[0].stride(0):
+            raise ValueError("k_srcs and v_srcs must share one dtype and row stride")
+    for t in qs:
+        if t.dtype != qs[0].dtype or t.stride(0) != qs[0].stride(0):
+            raise ValueError("qs must share one dtype and row stride")
+    ws_ptr, ws_bytes = 0, 0
+    if balance:
+        nbytes = max(attn_workspace(plan, round, c.heads, c.head_dim)[0] for c in caches)
+        if workspace is None and nbytes > 0:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=qs[0].device)
+        if workspace is not None:
+            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    cache_arr = (_lib.KvCache * n)(*[c.c for c in caches])
+
+    def ptrs(ts):
+        return (C.c_void_p * n)(*[t.data_ptr() if t is not None else 0 for t in ts])
+
+    _lib.check(_lib.load().wave_round(plan.handle, C.c_void_p(d_desc.data_ptr()), round, n, cache_arr,
+                                      ptrs(k_srcs), ptrs(v_srcs), _dtype_code(k_srcs[0]), k_srcs[0].stride(0),
+                                      ptrs(qs), _dtype_code(qs[0]), qs[0].stride(0), ptrs(outs_o),
+                                      ptrs(outs_l) if want_lse or lses is not None else None, float(scale),
+                                      C.c_void_p(ws_ptr), ws_bytes, _stream_ptr(stream)))
+    return outs_o, outs_l
 
 
 def splitkv_workspace_bytes(plan: Plan, round: int, heads: int, head_dim: int, num_splits: int = 0):

@@ -24,7 +24,8 @@ WAVE_KEY_TILE = 64
 
 EXPORTS = ("wave_plan", "wave_plan_view_get", "wave_plan_desc_size", "wave_plan_desc_pack",
            "wave_plan_destroy", "kv_write", "wave_attn_workspace", "wave_attn", "wave_attn_splitkv_workspace",
-           "wave_attn_splitkv", "qkv_project_workspace", "qkv_project", "chain_store", "wave_last_error")
+           "wave_round", "wave_attn_splitkv", "qkv_project_workspace", "qkv_project", "chain_store",
+           "wave_last_error")
 
 
 class PlanParams(C.Structure):
@@ -101,6 +102,11 @@ def load() -> C.CDLL:
                               C.c_void_p, C.c_int32, C.c_int64, C.c_void_p, C.c_void_p,
                               C.c_float, C.c_void_p, C.c_size_t, C.c_void_p]
     lib.wave_attn.restype = C.c_int32
+    P = C.POINTER(C.c_void_p)
+    lib.wave_round.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.POINTER(KvCache), P, P,
+                               C.c_int32, C.c_int64, P, C.c_int32, C.c_int64, P, P, C.c_float, C.c_void_p,
+                               C.c_size_t, C.c_void_p]
+    lib.wave_round.restype = C.c_int32
     lib.wave_attn_splitkv_workspace.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                                 C.POINTER(C.c_size_t), C.POINTER(C.c_int32)]
     lib.wave_attn_splitkv_workspace.restype = C.c_int32

@@ -10,6 +10,7 @@
 #include <mutex>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "balance.hpp"
 #include "kernels.hpp"
@@ -61,6 +62,41 @@ int32_t check_common(const wave_plan_t* plan, const void* d_desc, int32_t round,
     return set_error(WAVE_ERR_CAPACITY, f + ": lpad shorter than the plan's longest slot");
   if (cache->num_slots < p.num_phys_slots)
     return set_error(WAVE_ERR_CAPACITY, f + ": cache has fewer slots than the plan needs");
+  return WAVE_OK;
+}
+
+// Validates kv_write's arguments and fills its launch arguments (num_writes
+// = 0 for a round without writes, which launches nothing).
+int32_t kv_prepare(const wave_plan_t* plan, const void* d_desc, int32_t round, const wave_kv_cache* cache,
+                   const void* k_src, const void* v_src, int32_t src_dtype, int64_t src_row_stride, const char* fn,
+                   wave::KvWriteArgs& a) {
+  int32_t rc = check_common(plan, d_desc, round, cache, fn);
+  if (rc != WAVE_OK) return rc;
+  const std::string f(fn);
+  const wave::Plan& p = plan->p;
+  const int32_t w0 = p.round_write_begin[round], w1 = p.round_write_begin[round + 1];
+  a = wave::KvWriteArgs{};
+  if (w1 == w0) return WAVE_OK;
+  if (!k_src || !v_src) return set_error(WAVE_ERR_INVALID_ARG, f + ": null source");
+  if (src_dtype != WAVE_DTYPE_BF16 && src_dtype != WAVE_DTYPE_FP32)
+    return set_error(WAVE_ERR_UNSUPPORTED, f + ": src_dtype must be WAVE_DTYPE_BF16 or WAVE_DTYPE_FP32");
+  const int64_t row = static_cast<int64_t>(cache->heads) * cache->head_dim;
+  if (src_row_stride < row) return set_error(WAVE_ERR_INVALID_ARG, f + ": src_row_stride < heads*head_dim");
+  const int64_t esz = src_dtype == WAVE_DTYPE_FP32 ? 4 : 2;
+  if (!aligned16(k_src) || !aligned16(v_src) || (src_row_stride * esz) % 16 != 0)
+    return set_error(WAVE_ERR_UNSUPPORTED, f + ": sources and row stride must be 16-byte aligned");
+  const int32_t* desc = static_cast<const int32_t*>(d_desc);
+  a.writes = desc + p.desc[10] + static_cast<int64_t>(w0) * wave::kWriteStride;
+  a.num_writes = w1 - w0;
+  a.k = cache->k;
+  a.vt = cache->vt;
+  a.heads = cache->heads;
+  a.head_dim = cache->head_dim;
+  a.lpad = cache->lpad;
+  a.k_src = k_src;
+  a.v_src = v_src;
+  a.src_fp32 = src_dtype == WAVE_DTYPE_FP32;
+  a.src_row_stride = src_row_stride;
   return WAVE_OK;
 }
 
@@ -130,32 +166,9 @@ void wave_plan_destroy(wave_plan_t* plan) { delete plan; }
 int32_t kv_write(const wave_plan_t* plan, const void* d_desc, int32_t round, const wave_kv_cache* cache,
                  const void* k_src, const void* v_src, int32_t src_dtype, int64_t src_row_stride,
                  void* stream) {
-  int32_t rc = check_common(plan, d_desc, round, cache, "kv_write");
-  if (rc != WAVE_OK) return rc;
-  const wave::Plan& p = plan->p;
-  const int32_t w0 = p.round_write_begin[round], w1 = p.round_write_begin[round + 1];
-  if (w1 == w0) return ok();
-  if (!k_src || !v_src) return set_error(WAVE_ERR_INVALID_ARG, "kv_write: null source");
-  if (src_dtype != WAVE_DTYPE_BF16 && src_dtype != WAVE_DTYPE_FP32)
-    return set_error(WAVE_ERR_UNSUPPORTED, "kv_write: src_dtype must be WAVE_DTYPE_BF16 or WAVE_DTYPE_FP32");
-  const int64_t row = static_cast<int64_t>(cache->heads) * cache->head_dim;
-  if (src_row_stride < row) return set_error(WAVE_ERR_INVALID_ARG, "kv_write: src_row_stride < heads*head_dim");
-  const int64_t esz = src_dtype == WAVE_DTYPE_FP32 ? 4 : 2;
-  if (!aligned16(k_src) || !aligned16(v_src) || (src_row_stride * esz) % 16 != 0)
-    return set_error(WAVE_ERR_UNSUPPORTED, "kv_write: sources and row stride must be 16-byte aligned");
-  const int32_t* desc = static_cast<const int32_t*>(d_desc);
   wave::KvWriteArgs a{};
-  a.writes = desc + p.desc[10] + static_cast<int64_t>(w0) * wave::kWriteStride;
-  a.num_writes = w1 - w0;
-  a.k = cache->k;
-  a.vt = cache->vt;
-  a.heads = cache->heads;
-  a.head_dim = cache->head_dim;
-  a.lpad = cache->lpad;
-  a.k_src = k_src;
-  a.v_src = v_src;
-  a.src_fp32 = src_dtype == WAVE_DTYPE_FP32;
-  a.src_row_stride = src_row_stride;
+  const int32_t rc = kv_prepare(plan, d_desc, round, cache, k_src, v_src, src_dtype, src_row_stride, "kv_write", a);
+  if (rc != WAVE_OK) return rc;
   const hipError_t e = wave::launch_kv_write(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return set_error(WAVE_ERR_HIP, std::string("kv_write: ") + hipGetErrorString(e));
   return ok();
@@ -266,6 +279,33 @@ int32_t attn_common(const wave_plan_t* plan, const void* d_desc, int32_t round, 
   return WAVE_OK;
 }
 
+// wave_attn's checks plus its optional tail-balancing workspace.
+int32_t attn_prepare(const wave_plan_t* plan, const void* d_desc, int32_t round, const wave_kv_cache* cache,
+                     const void* q, int32_t q_dtype, int64_t q_row_stride, void* o, float* lse, float scale,
+                     void* workspace, size_t workspace_bytes, const char* fn, wave::AttnArgs& a) {
+  const int32_t rc = attn_common(plan, d_desc, round, cache, q, q_dtype, q_row_stride, o, lse, scale, fn, a);
+  if (rc != WAVE_OK) return rc;
+  if (!workspace) return WAVE_OK;
+  const std::string f(fn);
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+    return set_error(WAVE_ERR_INVALID_ARG, f + ": workspace must be 256-byte aligned");
+  const wave::TailSplit t = tail_for(plan, round, cache->heads, cache->head_dim, device_cus());
+  size_t lse_off = 0;
+  const size_t need = tail_bytes(t, cache->heads, cache->head_dim, &lse_off);
+  if (workspace_bytes < need)
+    return set_error(WAVE_ERR_CAPACITY, f + ": workspace smaller than wave_attn_workspace()");
+  if (t.items > 0) {
+    if (static_cast<int64_t>(a.num_work) * cache->heads * t.splits > INT32_MAX)
+      return set_error(WAVE_ERR_UNSUPPORTED, f + ": too many workgroups");
+    a.num_direct = a.num_work - t.items;
+    a.tail_splits = t.splits;
+    a.part_rows = t.items * WAVE_Q_TILE;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + lse_off);
+  }
+  return WAVE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -290,30 +330,45 @@ int32_t wave_attn(const wave_plan_t* plan, const void* d_desc, int32_t round, co
                   const void* q, int32_t q_dtype, int64_t q_row_stride, void* o, float* lse, float scale,
                   void* workspace, size_t workspace_bytes, void* stream) {
   wave::AttnArgs a;
-  const int32_t rc = attn_common(plan, d_desc, round, cache, q, q_dtype, q_row_stride, o, lse, scale,
-                                 "wave_attn", a);
+  const int32_t rc = attn_prepare(plan, d_desc, round, cache, q, q_dtype, q_row_stride, o, lse, scale, workspace,
+                                  workspace_bytes, "wave_attn", a);
   if (rc != WAVE_OK) return rc;
-  if (workspace) {
-    if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
-      return set_error(WAVE_ERR_INVALID_ARG, "wave_attn: workspace must be 256-byte aligned");
-    const wave::TailSplit t = tail_for(plan, round, cache->heads, cache->head_dim, device_cus());
-    size_t lse_off = 0;
-    const size_t need = tail_bytes(t, cache->heads, cache->head_dim, &lse_off);
-    if (workspace_bytes < need)
-      return set_error(WAVE_ERR_CAPACITY, "wave_attn: workspace smaller than wave_attn_workspace()");
-    if (t.items > 0) {
-      if (static_cast<int64_t>(a.num_work) * cache->heads * t.splits > INT32_MAX)
-        return set_error(WAVE_ERR_UNSUPPORTED, "wave_attn: too many workgroups");
-      a.num_direct = a.num_work - t.items;
-      a.tail_splits = t.splits;
-      a.part_rows = t.items * WAVE_Q_TILE;
-      a.part_o = static_cast<float*>(workspace);
-      a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + lse_off);
-    }
-  }
   const hipError_t e = wave::launch_wave_attn(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return set_error(WAVE_ERR_HIP, std::string("wave_attn: ") + hipGetErrorString(e));
   return ok();
+}
+
+int32_t wave_round(const wave_plan_t* plan, const void* d_desc, int32_t round, int32_t num_layers,
+                   const wave_kv_cache* caches, const void* const* k_src, const void* const* v_src, int32_t src_dtype,
+                   int64_t src_row_stride, const void* const* q, int32_t q_dtype, int64_t q_row_stride,
+                   void* const* o, float* const* lse, float scale, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  if (num_layers < 1 || !caches || !k_src || !v_src || !q || !o)
+    return set_error(WAVE_ERR_INVALID_ARG, "wave_round: num_layers < 1 or a null per-layer array");
+  try {
+    // Every layer's arguments are checked before anything is enqueued.
+    std::vector<wave::KvWriteArgs> kw(static_cast<size_t>(num_layers));
+    std::vector<wave::AttnArgs> at(static_cast<size_t>(num_layers));
+    for (int32_t l = 0; l < num_layers; ++l) {
+      const std::string fn = "wave_round (layer " + std::to_string(l) + ")";
+      int32_t rc = kv_prepare(plan, d_desc, round, &caches[l], k_src[l], v_src[l], src_dtype, src_row_stride,
+                              fn.c_str(), kw[l]);
+      if (rc != WAVE_OK) return rc;
+      rc = attn_prepare(plan, d_desc, round, &caches[l], q[l], q_dtype, q_row_stride, o[l], lse ? lse[l] : nullptr,
+                        scale, workspace, workspace_bytes, fn.c_str(), at[l]);
+      if (rc != WAVE_OK) return rc;
+    }
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int32_t l = 0; l < num_layers; ++l) {
+      hipError_t e = wave::launch_kv_write(kw[l], st);
+      if (e == hipSuccess) e = wave::launch_wave_attn(at[l], st);
+      if (e != hipSuccess)
+        return set_error(WAVE_ERR_HIP, "wave_round (layer " + std::to_string(l) + "): " + hipGetErrorString(e));
+    }
+    return ok();
+  } catch (const std::bad_alloc&) {
+    return set_error(WAVE_ERR_NOMEM, "wave_round: out of host memory");
+  }
 }
 
 int32_t wave_attn_splitkv_workspace(const wave_plan_t* plan, int32_t round, int32_t heads, int32_t head_dim,

@@ -209,6 +209,28 @@ int32_t wave_attn(const wave_plan_t* plan, const void* d_desc, int32_t round,
                   int64_t q_row_stride, void* o, float* lse, float scale,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* One wave round of every layer: for each layer l in order, kv_write of the
+ * round's fresh K/V into caches[l], then wave_attn of the round's nodes on
+ * that cache, all on `stream` with no host synchronisation (a round is one
+ * concurrent forward pass over the chunks in flight, with each chunk's K/V in
+ * the cache before the attention that reads it: Wave Forcing summary,
+ * mechanism paragraph; Wan-Streamer v0.2 abstract).
+ *   num_layers: >= 1; caches, k_src, v_src, q, o: arrays of num_layers
+ *               entries, one per layer, each as for kv_write / wave_attn;
+ *   lse: NULL, or an array of num_layers entries (entries may be NULL).
+ *   src_dtype, src_row_stride, q_dtype, q_row_stride, scale: shared by the
+ *               layers.
+ *   workspace: as for wave_attn (NULL, or >= wave_attn_workspace() bytes);
+ *               the layers reuse it one after another on `stream`.
+ * Every layer's arguments are checked before anything is enqueued; an error
+ * names the layer.  A launch error part-way leaves the earlier layers'
+ * launches enqueued.  Results equal those of the separate calls. */
+int32_t wave_round(const wave_plan_t* plan, const void* d_desc, int32_t round, int32_t num_layers,
+                   const wave_kv_cache* caches, const void* const* k_src, const void* const* v_src,
+                   int32_t src_dtype, int64_t src_row_stride, const void* const* q, int32_t q_dtype,
+                   int64_t q_row_stride, void* const* o, float* const* lse, float scale,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* Split-KV attention for short query chunks against long contexts (the
  * decode-shaped case: e.g. a chunk's 64 audio rows against tens of thousands
  * of cached keys, Wan-Streamer v0.2 abstract and "Latency-Preserving

@@ -280,6 +280,48 @@ def test_wan13b_k5_rollout_sampled(gpu_device, policy, layer):
     log(f"  {len(want)} nodes; last {s}")
 
 
+@pytest.mark.parametrize("balance", [True, False])
+def test_wave_round_equals_separate_calls(gpu_device, balance):
+    """wave_round (every layer of a round in one call on one stream, no host
+    sync) gives bitwise the outputs of kv_write + wave_attn per layer, and
+    matches the oracle on one layer's whole rollout."""
+    import torch
+    B, K, L, heads, hd, layers = 4, 2, 300, 2, 128, 3
+    log(f"wave_round: {layers} layers, balance={balance}")
+    plan = wv.wave_plan(B=B, K=K, policy=wv.PROGRESSIVE, sched=wv.WAVE, chunk_len=L)
+    desc = plan.upload(gpu_device)
+    inputs = [HostInputs(30, heads, hd, L, 0, layer=l) for l in range(layers)]
+
+    def mk():
+        return [wv.KVCache(plan.num_phys_slots, heads, hd, plan.lpad(), gpu_device, fill=float("nan"))
+                for _ in range(layers)]
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(gpu_device)
+
+    caches_a, caches_b = mk(), mk()
+    got = {}
+    for t in range(plan.num_rounds):
+        ws = plan.round_writes(t).tolist()
+        nodes = plan.round_nodes(t).tolist()
+        ks = [dev(np.concatenate([inp.kv(c, lv)[0] for (c, lv, _, _) in ws])) for inp in inputs]
+        vs = [dev(np.concatenate([inp.kv(c, lv)[1] for (c, lv, _, _) in ws])) for inp in inputs]
+        qs = [dev(np.concatenate([inp.q(n[0], n[1]) for n in nodes])) for inp in inputs]
+        oa, la = wv.wave_round(plan, desc, t, caches_a, ks, vs, qs, 1.0 / np.sqrt(hd), balance=balance)
+        for l in range(layers):
+            wv.kv_write(plan, desc, t, caches_b[l], ks[l], vs[l])
+            ob, lb = wv.wave_attn(plan, desc, t, caches_b[l], qs[l], 1.0 / np.sqrt(hd), balance=balance)
+            torch.cuda.synchronize()
+            assert torch.equal(oa[l], ob) and torch.equal(la[l], lb), (t, l)
+        o1, l1 = oa[1].float().cpu().numpy(), la[1].cpu().numpy()
+        for n in nodes:
+            got[(n[0], n[1])] = (o1[n[4]:n[4] + n[5]], l1[:, n[4]:n[4] + n[5]])
+    ref = oracle_rollout(B, K, wi.PROGRESSIVE, -1, L, 0, inputs[1], 1.0 / np.sqrt(hd))
+    assert set(ref) == set(got)
+    for key in ref:
+        compare(got[key][0], got[key][1], ref[key][0], ref[key][1], f"node {key}")
+
+
 SPLIT_GRID = [
     # policy, H, cond, L, query_len, heads, hd, splits
     (wi.PROGRESSIVE, -1, 0, 300, 0, 2, 128, 3),

@@ -213,6 +213,36 @@ def test_device_calls_validate_before_launch():
     assert kvw(src=C.c_void_p(0x10008)) == _lib.WAVE_ERR_UNSUPPORTED
 
 
+def test_wave_round_validates_every_layer_before_launch():
+    """wave_round checks every layer's arguments on the host before it enqueues
+    anything, and the error names the layer (no GPU needed: each call below
+    has an invalid layer, so nothing is launched)."""
+    lib = _lib.load()
+    pn = native(4, 2, op.PROGRESSIVE, op.WAVE, -1, 128, 0)
+    fake = 0x10000  # never dereferenced
+    good = _lib.KvCache(0x10000, 0x20000, 4, 2, 64, 128)
+    P = C.c_void_p * 2
+
+    def rnd(n=2, caches=(good, good), k=(fake, fake), q=(fake, fake), o=(fake, fake), qd=0, round_=0,
+            scale=0.125):
+        arr = (_lib.KvCache * 2)(*caches)
+        return lib.wave_round(pn.handle, C.c_void_p(fake), round_, n, arr, P(*k), P(fake, fake), 0, 128, P(*q), qd,
+                              128, P(*o), None, scale, None, 0, C.c_void_p(0))
+
+    assert rnd(n=0) == _lib.WAVE_ERR_INVALID_ARG
+    assert lib.wave_round(pn.handle, C.c_void_p(fake), 0, 2, None, P(fake, fake), P(fake, fake), 0, 128,
+                          P(fake, fake), 0, 128, P(fake, fake), None, 0.125, None, 0,
+                          C.c_void_p(0)) == _lib.WAVE_ERR_INVALID_ARG
+    assert rnd(q=(fake, 0)) == _lib.WAVE_ERR_INVALID_ARG and b"layer 1" in lib.wave_last_error()
+    assert rnd(k=(fake, 0)) == _lib.WAVE_ERR_INVALID_ARG and b"layer 1" in lib.wave_last_error()
+    assert rnd(o=(0, fake)) == _lib.WAVE_ERR_INVALID_ARG and b"layer 0" in lib.wave_last_error()
+    short = _lib.KvCache(0x10000, 0x20000, 4, 2, 64, 64)
+    assert rnd(caches=(good, short)) == _lib.WAVE_ERR_CAPACITY and b"layer 1" in lib.wave_last_error()
+    assert rnd(round_=9) == _lib.WAVE_ERR_INVALID_ARG
+    assert rnd(qd=7) == _lib.WAVE_ERR_UNSUPPORTED
+    assert rnd(scale=float("inf")) == _lib.WAVE_ERR_INVALID_ARG
+
+
 def test_tail_balancing_choice_and_workspace_checks():
     """wave_attn's tail balancing: the memoised choice for the Wan2.1-1.3B round-6
     shape (95 work items x 12 heads on 256 compute units) cuts some trailing
