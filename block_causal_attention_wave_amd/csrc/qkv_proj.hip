@@ -20,6 +20,9 @@
 //                     k-steps in flight, one barrier per k-step), and an
 //                     epilogue that scales, rounds and scatters the tile
 //                     through LDS.
+//   qkv_gemm_wide_kernel  the same with 256-column tiles (8 waves of 128x64,
+//                     two 64 KiB stages), for model dims that are multiples
+//                     of 256: fewer operand reads and tile bytes per flop.
 //   chain_store_kernel  copies each node's output rows to its chunk's state.
 #include <hip/hip_runtime.h>
 
@@ -273,6 +276,219 @@ __global__ __launch_bounds__(THREADS, 2) void qkv_gemm_kernel(ProjArgs a) {
   }
 }
 
+// Wide tiles, for model dims that are multiples of 256: one workgroup per
+// (node, 256-token tile, 256-column tile), 8 waves of 128x64.  Per 16-deep
+// substep a wave reads 6 operand fragments for 8 MFMAs (4 for 4 above), and
+// a tile loads 128 bytes of A and W per 256 * 256 * 2 flops (against 192).
+// Two 64 KiB stages: k-step ks+1 streams in while ks is multiplied.
+namespace wide {
+constexpr int TM = 256, TN = 256, TK = 64, NSTAGE = 2;
+constexpr int ROW_BYTES = TK * 2;
+constexpr int A_BYTES = TM * ROW_BYTES;
+constexpr int W_BYTES = TN * ROW_BYTES;
+constexpr int STAGE_BYTES = A_BYTES + W_BYTES;
+constexpr int A_LOADS = A_BYTES / (THREADS * 16);
+constexpr int W_LOADS = W_BYTES / (THREADS * 16);
+constexpr int OUT_PITCH_R = (TN + 8) * 2;
+constexpr int OUT_PITCH_C = (TM + 8) * 2;
+constexpr int LDS_BYTES = TM * OUT_PITCH_R > NSTAGE * STAGE_BYTES ? TM * OUT_PITCH_R : NSTAGE * STAGE_BYTES;
+static_assert(TN * OUT_PITCH_C <= LDS_BYTES, "column-major staging fits");
+static_assert(A_LOADS + W_LOADS <= 15, "vmcnt immediate");
+}  // namespace wide
+
+template <int HD>
+__global__ __launch_bounds__(THREADS, 1) void qkv_gemm_wide_kernel(ProjArgs a) {
+  using wide::TM;
+  using wide::TN;
+  using wide::TK;
+  using wide::ROW_BYTES;
+  using wide::A_BYTES;
+  using wide::STAGE_BYTES;
+  using wide::A_LOADS;
+  using wide::W_LOADS;
+  using wide::OUT_PITCH_R;
+  using wide::OUT_PITCH_C;
+  __shared__ __attribute__((aligned(1024))) char lds[wide::LDS_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wv >> 2, wc = wv & 3;  // this wave's 128x64 block of the tile
+  // Tile order as in qkv_gemm_kernel: contiguous tile ranges per XCD, groups
+  // of 4 row tiles x all column tiles inside a node.
+  int b = blockIdx.x;
+  {
+    const int per_xcd = (int)(gridDim.x / 8);
+    if (b < per_xcd * 8) b = (b % 8) * per_xcd + b / 8;
+  }
+  const int per_node = a.row_tiles * a.col_tiles;
+  const int node = a.node_begin + b / per_node;
+  int rt, ct;
+  {
+    constexpr int G = 4;
+    const int r = b % per_node;
+    const int full = a.row_tiles / G;
+    const int gsz = G * a.col_tiles;
+    if (r < full * gsz) {
+      ct = (r % gsz) / G;
+      rt = (r / gsz) * G + r % G;
+    } else {
+      const int rem = a.row_tiles - full * G, rr = r - full * gsz;
+      ct = rr / rem;
+      rt = full * G + rr % rem;
+    }
+  }
+  const int32_t* nd = a.nodes + kDescNodeWords * node;
+  const int q_offset = nd[0], L = nd[1], chunk = nd[4];
+  const int phys = a.ctx[2 * (nd[2] + nd[3] - 1)];  // the node's own slot: last in its gather list
+  const int D = a.model_dim;
+  const int r0 = rt * TM, c0 = ct * TN;
+
+  const char* abase = static_cast<const char*>(a.x) +
+                      ((a.x_chunk ? (int64_t)chunk * a.chunk_rows : (int64_t)q_offset) * D) * 2;
+  const char* wbase = static_cast<const char*>(a.w) + (int64_t)c0 * D * 2;
+  uint32_t aoff[A_LOADS], woff[W_LOADS];
+#pragma unroll
+  for (int n = 0; n < A_LOADS; ++n) {
+    const int off = (wv * A_LOADS + n) * 1024 + lane * 16;
+    const int row = off / ROW_BYTES;
+    const int lc = ((off % ROW_BYTES) / 16) ^ swz(row);
+    aoff[n] = (uint32_t)(((int64_t)min(r0 + row, L - 1) * D + lc * 8) * 2);
+  }
+#pragma unroll
+  for (int n = 0; n < W_LOADS; ++n) {
+    const int off = (wv * W_LOADS + n) * 1024 + lane * 16;
+    const int row = off / ROW_BYTES;
+    const int lc = ((off % ROW_BYTES) / 16) ^ swz(row);
+    woff[n] = (uint32_t)(((int64_t)row * D + lc * 8) * 2);
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+  auto issue = [&](int ks, int stage) {
+    const char* ab = abase + (int64_t)ks * TK * 2;
+    const char* wb = wbase + (int64_t)ks * TK * 2;
+    const uint32_t sa = lds0 + stage * STAGE_BYTES, sw = sa + A_BYTES;
+#pragma unroll
+    for (int n = 0; n < A_LOADS; ++n) load_lds16(sa + (wv * A_LOADS + n) * 1024, ab, aoff[n]);
+#pragma unroll
+    for (int n = 0; n < W_LOADS; ++n) load_lds16(sw + (wv * W_LOADS + n) * 1024, wb, woff[n]);
+  };
+  auto barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  constexpr int kWaitExp = (0x7 << 4) | (0xF << 8);  // wait on vmcnt only
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  // Two stages: after the barrier of k-step ks every wave is done with ks-1,
+  // whose stage receives ks+1 while ks is multiplied.
+  const int nk = D / TK;
+  issue(0, 0);
+  int stage = 0;
+  for (int ks = 0; ks < nk; ++ks) {
+    __builtin_amdgcn_s_waitcnt(kWaitExp);  // this thread's loads of k-step ks have landed
+    barrier();
+    if (ks + 1 < nk) issue(ks + 1, stage ^ 1);
+    const char* sa = lds + stage * STAGE_BYTES;
+    const char* sw = sa + A_BYTES;
+    auto frags = [&](int s, bf16x8 (&af)[4], bf16x8 (&bf)[2]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = wr * 128 + i * 32 + (lane & 31);
+        af[i] = *reinterpret_cast<const bf16x8*>(sa + row * ROW_BYTES + (((2 * s + (lane >> 5)) ^ swz(row)) * 16));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = wc * 64 + j * 32 + (lane & 31);
+        bf[j] = *reinterpret_cast<const bf16x8*>(sw + row * ROW_BYTES + (((2 * s + (lane >> 5)) ^ swz(row)) * 16));
+      }
+    };
+    bf16x8 af[2][4], bf[2][2];
+    frags(0, af[0], bf[0]);
+#pragma unroll
+    for (int s = 0; s < TK / 16; ++s) {
+      if (s + 1 < TK / 16) frags(s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][i], bf[s & 1][j], acc[i][j], 0, 0, 0);
+    }
+    // Keep that order: reads of substeps 0 and 1, then (MFMAs of s, reads of s+2).
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+#pragma unroll
+    for (int s = 0; s < TK / 16 - 2; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    stage ^= 1;
+  }
+  barrier();  // the epilogue reuses the stages
+
+  // Epilogue as in qkv_gemm_kernel: scale by 1/rms, round, stage in LDS
+  // (column-major for V), then 16-byte stores to Q, K or V^T.
+  const int part = c0 / D;  // 0: Q, 1: K, 2: V (D is a multiple of TN)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int row0 = wr * 128 + i * 32 + 8 * g + 4 * (lane >> 5);
+      float sc[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = r0 + row0 + e;
+        sc[e] = r < L ? a.row_scale[q_offset + r] : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = wc * 64 + j * 32 + (lane & 31);
+        if (part == 2) {
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[i][j][4 * g + e] * sc[e]);
+          *reinterpret_cast<bf16x4*>(lds + col * OUT_PITCH_C + row0 * 2) = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            *reinterpret_cast<__bf16*>(lds + (row0 + e) * OUT_PITCH_R + col * 2) = (__bf16)(acc[i][j][4 * g + e] * sc[e]);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int heads = a.heads, lpad = a.lpad;
+  for (int id = tid; id < TM * (TN / 8); id += THREADS) {
+    if (part == 2) {
+      const int col = id / (TM / 8), tok = r0 + (id % (TM / 8)) * 8;
+      if (tok >= lpad) continue;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + col * OUT_PITCH_C + (tok - r0) * 2);
+      const int h = (c0 - 2 * D + col) / HD, dd = (c0 - 2 * D + col) % HD;
+      __bf16* dst = static_cast<__bf16*>(a.vt) + (((int64_t)phys * heads + h) * HD + dd) * lpad + tok;
+      *reinterpret_cast<u32x4*>(dst) = v;
+    } else {
+      const int row = id / (TN / 8), cc = (id % (TN / 8)) * 8;
+      const int r = r0 + row;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * OUT_PITCH_R + cc * 2);
+      if (part == 0) {
+        if (r >= L) continue;
+        __bf16* dst = static_cast<__bf16*>(a.q) + (int64_t)(q_offset + r) * D + c0 + cc;
+        *reinterpret_cast<u32x4*>(dst) = v;
+      } else {
+        if (r >= lpad) continue;
+        const int h = (c0 - D + cc) / HD, dd = (c0 - D + cc) % HD;
+        __bf16* dst = static_cast<__bf16*>(a.k) + (((int64_t)phys * heads + h) * lpad + r) * HD + dd;
+        *reinterpret_cast<u32x4*>(dst) = v;
+      }
+    }
+  }
+}
+
 // state[chunk rows] = o[node rows] for every node of the round: grid (row
 // chunks of 256 x 8 elements, nodes).
 __global__ __launch_bounds__(256) void chain_store_kernel(StoreArgs a) {
@@ -295,6 +511,15 @@ hipError_t launch_qkv_project(const ProjArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(row_scale_kernel, sgrid, dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.model_dim % wide::TN == 0) {
+    // 256-wide column tiles: a tile never straddles the Q / K / V parts
+    ProjArgs w = a;
+    w.col_tiles = 3 * a.model_dim / wide::TN;
+    dim3 grid((unsigned)(w.num_nodes * w.row_tiles * w.col_tiles));
+    if (a.head_dim == 128) hipLaunchKernelGGL(qkv_gemm_wide_kernel<128>, grid, dim3(THREADS), 0, stream, w);
+    else hipLaunchKernelGGL(qkv_gemm_wide_kernel<64>, grid, dim3(THREADS), 0, stream, w);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)(a.num_nodes * a.row_tiles * a.col_tiles));
   if (a.head_dim == 128) hipLaunchKernelGGL(qkv_gemm_kernel<128>, grid, dim3(THREADS), 0, stream, a);
   else hipLaunchKernelGGL(qkv_gemm_kernel<64>, grid, dim3(THREADS), 0, stream, a);

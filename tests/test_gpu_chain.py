@@ -59,7 +59,8 @@ def gpu_chain(plan, B, L, heads, hd, noise, weights, scale, device, balance=Fals
 
 
 @pytest.mark.parametrize("heads,hd,L,layout", [(2, 64, 300, wv.X_CHUNK), (1, 128, 129, wv.X_ROUND),
-                                               (3, 128, 200, wv.X_CHUNK), (4, 64, 64, wv.X_ROUND)])
+                                               (3, 128, 200, wv.X_CHUNK), (4, 64, 64, wv.X_ROUND),
+                                               (2, 128, 300, wv.X_CHUNK), (4, 128, 520, wv.X_ROUND)])
 def test_qkv_project_parity(gpu_device, heads, hd, L, layout):
     """Q, K and V^T of one round against oracle.chain.project on the same bf16
     inputs, slot tails exactly zero, slots of other rounds untouched.  Bound
@@ -139,6 +140,7 @@ CHAIN_GRID = [
     (wi.PROGRESSIVE, 3, 2, 160, 2, 64, 2),
     (wi.SAME_LEVEL, 4, 2, 130, 1, 128, 1),
     (wi.CLEAN, 3, 3, 96, 2, 64, 2),
+    (wi.PROGRESSIVE, 3, 2, 200, 4, 64, 2),
 ]
 
 
