@@ -99,6 +99,41 @@ def test_small_grid_parity(gpu_device, policy, H, cond, L, heads, hd, dtype, bal
         compare(got[key][0], got[key][1], ref[key][0], ref[key][1], f"node {key}")
 
 
+def _random_config(i):
+    """Seeded small configuration i: chunks, levels, policy, history cap,
+    conditioning length, chunk length (single tokens and ragged tiles
+    included), decode-shaped query length, heads, head dim, source dtype,
+    schedule, and the attention path (balanced, plain, split-KV)."""
+    rng = np.random.default_rng(9000 + i)
+    B, K = int(rng.integers(1, 9)), int(rng.integers(1, 6))
+    policy, H = int(rng.integers(0, 3)), int(rng.choice([-1, -1, 0, 1, 2, 4]))
+    cond, L = int(rng.choice([0, 0, 1, 17, 64, 130])), int(rng.choice([1, 7, 64, 65, 129, 200, 300]))
+    qlen = int(rng.choice([0, 0, 0, 1, 8, 33]))
+    qlen = 0 if qlen >= L else qlen
+    heads, hd = int(rng.integers(1, 4)), int(rng.choice([64, 128]))
+    dtype, path = str(rng.choice(["fp32", "bf16"])), str(rng.choice(["balanced", "plain", "split0", "split3"]))
+    sched = int(rng.choice([wv.SERIAL, wv.WAVE]))
+    return B, K, policy, H, cond, L, qlen, heads, hd, dtype, path, sched
+
+
+@pytest.mark.parametrize("i", range(32))
+def test_random_small_configs_parity(gpu_device, i):
+    """Every node of 32 seeded small rollouts against the oracle's serial rollout."""
+    B, K, policy, H, cond, L, qlen, heads, hd, dtype, path, sched = _random_config(i)
+    log(f"config {i}: B={B} K={K} policy={policy} H={H} cond={cond} L={L} query_len={qlen} heads={heads} "
+        f"hd={hd} {dtype} {path} sched={sched}")
+    plan = wv.wave_plan(B=B, K=K, policy=policy, sched=sched, chunk_len=L, cond_len=cond, history_cap=H,
+                        query_len=qlen)
+    inp = HostInputs(200 + i, heads, hd, L, cond, bf16=(dtype == "bf16"), query_len=qlen)
+    scale = 1.0 / np.sqrt(hd)
+    splits = {"split0": 0, "split3": 3}.get(path)
+    got = gpu_rollout(plan, inp, gpu_device, scale, src_dtype=dtype, splits=splits, balance=(path == "balanced"))
+    ref = oracle_rollout(B, K, policy, H, L, cond, inp, scale, query_len=qlen)
+    assert set(got) == set(ref)
+    for key in ref:
+        compare(got[key][0], got[key][1], ref[key][0], ref[key][1], f"node {key}")
+
+
 @pytest.mark.parametrize("policy", [wi.CLEAN, wi.SAME_LEVEL, wi.PROGRESSIVE])
 def test_serial_and_wave_schedules_bitwise_equal(gpu_device, policy):
     B, K, L, heads, hd, cond = 5, 3, 200, 2, 128, 40
