@@ -717,10 +717,8 @@ hipError_t launch_combine(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-#ifndef WAVE_ATTN_WAVES
-#define WAVE_ATTN_WAVES 8
-#endif
-constexpr int kWaves = WAVE_ATTN_WAVES;
+// 8 waves of 32 query rows: two waves per SIMD at 216 VGPRs.
+constexpr int kWaves = 8;
 constexpr int kQB = kQTile / (32 * kWaves);
 
 }  // namespace
