@@ -307,6 +307,25 @@ def test_poisoned_slots_are_rewritten_before_any_later_read():
     assert reused > 0 and pn.num_phys_slots < len(pn.writes)
 
 
+@pytest.mark.parametrize("cond", [0, 512])
+def test_capped_history_cache_does_not_grow_with_chunks(cond):
+    """With a history cap the rolling cache's capacity is set by H and K, not by
+    the video's length: B = 28 (the long-video workload) and B = 4000 need the
+    same number of physical slots; the long plan keeps B+K-1 rounds and builds
+    in well under the time of one round of attention."""
+    import time
+    short = native(28, 4, op.PROGRESSIVE, op.WAVE, 6, 4680, cond)
+    t0 = time.perf_counter()
+    long_ = native(4000, 4, op.PROGRESSIVE, op.WAVE, 6, 4680, cond)
+    elapsed = time.perf_counter() - t0
+    assert long_.num_rounds == 4000 + 4 - 1
+    ref = op.oracle_plan(op.Params(28, 4, op.PROGRESSIVE, op.WAVE, 6, 4680, cond, 0))
+    assert long_.num_phys_slots == short.num_phys_slots == ref["num_phys_slots"]
+    if cond == 0:
+        assert ref["num_phys_slots"] == 11  # the long-video workload's capacity per layer
+    assert elapsed < 10.0
+
+
 def test_splitkv_auto_split_count_fills_one_dispatch_wave():
     """num_splits = 0: the most splits whose workgroups (items x heads x splits)
     fit 256 compute units in one dispatch wave (the device count falls back to
