@@ -134,6 +134,25 @@ def test_random_small_configs_parity(gpu_device, i):
         compare(got[key][0], got[key][1], ref[key][0], ref[key][1], f"node {key}")
 
 
+@pytest.mark.parametrize("splits", [None, 0])
+def test_long_slots_parity(gpu_device, splits):
+    """Chunks of 70,000 tokens (ragged: 1094 key tiles per slot, up to 210,000
+    keys per gather list), whole rollout, sampled rows against the oracle;
+    through wave_attn and through split-KV."""
+    B, K, L, heads, hd = 3, 2, 70000, 1, 128
+    log(f"long slots L={L} splits={splits}")
+    plan = wv.wave_plan(B=B, K=K, policy=wv.PROGRESSIVE, sched=wv.WAVE, chunk_len=L)
+    inp = HostInputs(41, heads, hd, L, 0, bf16=True)
+    scale = 1.0 / np.sqrt(hd)
+    got = gpu_rollout(plan, inp, gpu_device, scale, src_dtype="bf16", splits=splits)
+    rows = sample_rows(L, 96)
+    ref = oracle_rollout(B, K, wi.PROGRESSIVE, -1, L, 0, inp, scale, rows=lambda c, lv: rows)
+    assert set(got) == set(ref)
+    for key in ref:
+        s = compare(got[key][0][rows], got[key][1][:, rows], ref[key][0], ref[key][1], f"node {key}")
+    log(f"  last node {s}")
+
+
 @pytest.mark.parametrize("policy", [wi.CLEAN, wi.SAME_LEVEL, wi.PROGRESSIVE])
 def test_serial_and_wave_schedules_bitwise_equal(gpu_device, policy):
     B, K, L, heads, hd, cond = 5, 3, 200, 2, 128, 40
