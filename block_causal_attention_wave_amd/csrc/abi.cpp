@@ -58,6 +58,11 @@ int32_t check_common(const wave_plan_t* plan, const void* d_desc, int32_t round,
   if (cache->heads < 1 || cache->heads > 65535) return set_error(WAVE_ERR_INVALID_ARG, f + ": heads out of range");
   if (cache->lpad < 1 || cache->lpad % WAVE_KEY_TILE != 0)
     return set_error(WAVE_ERR_INVALID_ARG, f + ": lpad must be a positive multiple of WAVE_KEY_TILE");
+  // The attention kernel addresses a lane's share of a V^T tile with a 32-bit
+  // byte offset from the tile's first key: up to ((head_dim-1)*lpad + 56)*2
+  // plus the 16 bytes it loads.
+  if (static_cast<int64_t>(cache->head_dim - 1) * cache->lpad * 2 + 2 * WAVE_KEY_TILE > INT32_MAX)
+    return set_error(WAVE_ERR_UNSUPPORTED, f + ": lpad too long for 32-bit V^T tile offsets");
   if (cache->lpad < p.max_slot_len)
     return set_error(WAVE_ERR_CAPACITY, f + ": lpad shorter than the plan's longest slot");
   if (cache->num_slots < p.num_phys_slots)

@@ -150,8 +150,10 @@ void wave_plan_destroy(wave_plan_t* plan);
  *   k : bf16 [num_slots][heads][lpad][head_dim]  (token-major per head)
  *   vt: bf16 [num_slots][heads][head_dim][lpad]  (V transposed per head, so
  *       the P.V contraction streams keys contiguously)
- * lpad >= the plan's max_slot_len, a multiple of WAVE_KEY_TILE.  Tokens
- * [len, lpad) of a written slot are zero. */
+ * lpad >= the plan's max_slot_len, a multiple of WAVE_KEY_TILE, and
+ * (head_dim-1)*lpad*2 + 2*WAVE_KEY_TILE <= INT32_MAX (about 8.4 M tokens at
+ * head_dim 128; WAVE_ERR_UNSUPPORTED above).  Tokens [len, lpad) of a
+ * written slot are zero. */
 typedef struct wave_kv_cache {
   void* k;
   void* vt;

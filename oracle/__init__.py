@@ -24,6 +24,9 @@ Contents
     node consuming its previous node's last-layer attention output.
 
 Pins (values this oracle is checked against, other than itself) live in
-``tests/test_oracle_*.py`` and ``tests/golden/``.  Every function here is
-pinned; none is "parity unpinned".
+``tests/test_oracle_*.py`` and ``tests/golden/``: for the planner, closed-form
+round counts, brute-force minimality, structural invariants and hand-worked
+plans (pipelined, serial, same-level, clean, conditioned and history-capped)
+down to physical slot ids; for attention, library routines, closed forms and
+invariants.  Every function here is pinned; none is "parity unpinned".
 """

@@ -9,6 +9,11 @@
 * Slot allocation: no two live slots share an id, and the capacity equals the
   largest number of slots live at once (greedy interval colouring in order of
   start time is optimal).
+* Worked plans (``tests/golden/plan_*.txt``, each worked by hand from Table 1
+  and Figure 2 of the arXiv 2609.22283 listing and the stated readings):
+  pipelined progressive, serial progressive (the round of each refresh),
+  same-level, clean, conditioned (conditioning slot ids before latent ones)
+  and history-capped plans, node by node down to physical slot ids.
 """
 import itertools
 import os
@@ -197,35 +202,110 @@ def test_wave_rounds_minimal_bruteforce(B, K, policy):
     assert op.oracle_plan(p)["num_rounds"] == _min_rounds_bruteforce(p)
 
 
+def _slot(tok):
+    cl, ph = tok.split("@")
+    a, b = cl.split(".")
+    return (int(a), op.COND if b == "C" else int(b), int(ph))
+
+
 def _parse_plan_fixture(name):
+    """Rows (round, kind, chunk, level, writes, ctx) of a worked-plan fixture.
+
+    Two line formats: ``t kind c lv pid : ctx...`` (one written slot, given
+    by its physical id) and ``t kind c lv : writes... : ctx...``."""
     rows = []
     with open(os.path.join(GOLD, name)) as f:
         for line in f:
             if line.startswith("#") or not line.strip():
                 continue
-            head, tail = line.split(":")
-            t, kind, c, lv, pid = head.split()
-            refs = []
-            for tok in tail.split():
-                cl, ph = tok.split("@")
-                a, b = cl.split(".")
-                refs.append((int(a), int(b), int(ph)))
-            rows.append((int(t), kind, int(c), int(lv), int(pid), refs))
+            parts = line.split(":")
+            head = parts[0].split()
+            t, kind, c, lv = int(head[0]), head[1], int(head[2]), int(head[3])
+            if len(parts) == 2:
+                writes = [(c, lv, int(head[4]))]
+            else:
+                writes = [_slot(tok) for tok in parts[1].split()]
+            refs = [_slot(tok) for tok in parts[-1].split()]
+            rows.append((t, kind, c, lv, writes, refs))
     return rows
 
 
-def test_tiny_progressive_worked_plan():
-    pl = op.oracle_plan(P(4, 2, op.PROGRESSIVE, op.WAVE, L=128))
-    rows = _parse_plan_fixture("plan_tiny_progressive.txt")
-    assert pl["num_rounds"] == 5 and pl["num_phys_slots"] == 4
+# fixture -> (params, rounds, physical slots)
+PLAN_FIXTURES = {
+    "plan_tiny_progressive.txt": (P(4, 2, op.PROGRESSIVE, op.WAVE, L=128), 5, 4),
+    "plan_serial_progressive.txt": (P(4, 2, op.PROGRESSIVE, op.SERIAL, L=128), 8, 5),
+    "plan_same_level.txt": (P(3, 2, op.SAME_LEVEL, op.WAVE, L=128), 4, 5),
+    "plan_clean.txt": (P(3, 2, op.CLEAN, op.WAVE, L=128), 6, 3),
+    "plan_conditioned.txt": (P(3, 2, op.SAME_LEVEL, op.WAVE, L=128, cond=32), 4, 8),
+    "plan_capped_progressive.txt": (P(4, 2, op.PROGRESSIVE, op.WAVE, H=1, L=128), 5, 4),
+}
+
+
+def check_plan_fixture(name, pl):
+    """Assert that plan `pl` (oracle dict layout) is the worked plan `name`."""
+    params, rounds, slots = PLAN_FIXTURES[name]
+    rows = _parse_plan_fixture(name)
+    assert pl["num_rounds"] == rounds and pl["num_phys_slots"] == slots
     assert len(rows) == len(pl["nodes"])
     for row, n in zip(rows, pl["nodes"]):
-        t, kind, c, lv, pid, refs = row
-        assert (n[3], n[2], n[0], n[1]) == (t, op.REFRESH if kind == "R" else op.UPDATE, c, lv)
-        w = pl["writes"][n[8]:n[8] + n[9]]
-        assert [x[2] for x in w] == [pid]
-        got = [(x[0], x[1], x[2]) for x in pl["ctx"][n[6]:n[6] + n[7]]]
-        assert got == refs
+        t, kind, c, lv, writes, refs = row
+        assert (n[3], n[2], n[0], n[1]) == (t, op.REFRESH if kind == "R" else op.UPDATE, c, lv), row
+        assert [(x[0], x[1], x[2]) for x in pl["writes"][n[8]:n[8] + n[9]]] == writes, row
+        assert [(x[0], x[1], x[2]) for x in pl["ctx"][n[6]:n[6] + n[7]]] == refs, row
+        for x in pl["ctx"][n[6]:n[6] + n[7]]:
+            assert x[3] == (params.cond_len if x[1] == op.COND else params.chunk_len)
+
+
+@pytest.mark.parametrize("name", sorted(PLAN_FIXTURES))
+def test_worked_plans(name):
+    check_plan_fixture(name, op.oracle_plan(PLAN_FIXTURES[name][0]))
+
+
+def test_tiny_progressive_worked_plan():
+    check_plan_fixture("plan_tiny_progressive.txt", op.oracle_plan(P(4, 2, op.PROGRESSIVE, op.WAVE, L=128)))
+
+
+def _fixtures_fail():
+    for name in PLAN_FIXTURES:
+        try:
+            check_plan_fixture(name, op.oracle_plan(PLAN_FIXTURES[name][0]))
+        except AssertionError:
+            return True
+    return False
+
+
+def test_planted_plan_convention_slips_are_caught(monkeypatch):
+    """Slips in the two plan conventions that every structural pin tolerates
+    -- the serial refresh one round late (still a legal plan: the refresh and
+    its first reader share a round, lower chunk first), and the conditioning
+    slot allocated after the latent slot (still a valid allocation with the
+    same capacity) -- each break a worked-plan fixture."""
+    def late_refresh(p, per_chunk):
+        for i in range(p.B):
+            for n in per_chunk[i]:
+                n.round = i * p.K + p.K - n.level if n.kind == op.UPDATE else (i + 1) * p.K + 1
+        return p.B * p.K
+
+    monkeypatch.setattr(op, "_schedule_serial", late_refresh)
+    # oracle_plan runs check_legal: the slipped plan is still legal, so only
+    # a worked plan can catch it.
+    op.oracle_plan(P(4, 2, op.PROGRESSIVE, op.SERIAL, L=128))
+    assert _fixtures_fail()
+    monkeypatch.undo()
+
+    orig = op.build_nodes
+
+    def latent_first(p):
+        per_chunk = orig(p)
+        for lst in per_chunk.values():
+            for n in lst:
+                n.writes = list(reversed(n.writes))
+        return per_chunk
+
+    monkeypatch.setattr(op, "build_nodes", latent_first)
+    assert _fixtures_fail()
+    monkeypatch.undo()
+    assert not _fixtures_fail()
 
 
 def test_planted_mistakes_are_caught(monkeypatch):

@@ -16,6 +16,8 @@ import block_causal_attention_wave_amd as wv
 from oracle import plan as op
 from wave_inputs import WORKLOADS
 
+import test_oracle_plan as worked  # hand-worked plan fixtures and their checker
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
@@ -73,6 +75,17 @@ def test_planner_query_len_matches_oracle(query_len, pol):
         assert pn.round_q_rows[t] == query_len * (ne - nb)
         items = pn.work[pn.round_work_begin[t]:pn.round_work_begin[t + 1]]
         assert int(items[:, 2].sum()) == query_len * (ne - nb)
+
+
+@pytest.mark.parametrize("name", sorted(worked.PLAN_FIXTURES))
+def test_planner_matches_worked_plans(name):
+    """The native planner reproduces every hand-worked plan fixture."""
+    prm = worked.PLAN_FIXTURES[name][0]
+    pn = native(prm.B, prm.K, prm.policy, prm.sched, prm.history_cap, prm.chunk_len, prm.cond_len)
+    pl = {"num_rounds": pn.num_rounds, "num_phys_slots": pn.num_phys_slots,
+          "nodes": [tuple(x) for x in pn.nodes.tolist()], "ctx": [tuple(x) for x in pn.ctx.tolist()],
+          "writes": [tuple(x) for x in pn.writes.tolist()]}
+    worked.check_plan_fixture(name, pl)
 
 
 def test_workload_capacities_and_rounds():
@@ -184,6 +197,21 @@ def test_device_calls_validate_before_launch():
     assert attn(cache_=_lib.KvCache(0x10000, 0x20000, 4, 2, 96, 128)) == _lib.WAVE_ERR_UNSUPPORTED
     assert attn(cache_=_lib.KvCache(0x10000, 0x20000, 4, 2, 64, 100)) == _lib.WAVE_ERR_INVALID_ARG
     assert attn(cache_=_lib.KvCache(0, 0x20000, 4, 2, 64, 128)) == _lib.WAVE_ERR_INVALID_ARG
+    # 32-bit per-lane V^T tile offsets: (head_dim-1)*lpad*2 + 128 must fit in int32
+    lim128 = (2**31 - 1 - 128) // (127 * 2) // 64 * 64
+    lim64 = (2**31 - 1 - 128) // (63 * 2) // 64 * 64
+    for hd, lim in ((128, lim128), (64, lim64)):
+        pbig = _lib.KvCache(0x10000, 0x20000, 4, 2, hd, lim + 64)
+        assert lib.wave_attn(pn.handle, fake, 0, C.byref(pbig), fake, 0, 2 * hd, fake, None, 0.1, None, 0,
+                             stream) == _lib.WAVE_ERR_UNSUPPORTED
+        assert b"32-bit" in lib.wave_last_error()
+        assert lib.kv_write(pn.handle, fake, 0, C.byref(pbig), fake, fake, 0, 2 * hd,
+                            stream) == _lib.WAVE_ERR_UNSUPPORTED
+        # the largest accepted lpad passes this check (and fails later, on the null q)
+        ok = _lib.KvCache(0x10000, 0x20000, 4, 2, hd, lim)
+        assert lib.wave_attn(pn.handle, fake, 0, C.byref(ok), None, 0, 2 * hd, fake, None, 0.1, None, 0,
+                             stream) == _lib.WAVE_ERR_INVALID_ARG
+        assert b"null q" in lib.wave_last_error()
     assert b"capacity" in lib.wave_last_error() or len(lib.wave_last_error()) > 0
     pn128 = native(4, 2, op.PROGRESSIVE, op.WAVE, -1, 128, 0, q_tile=128)
     assert lib.wave_attn(pn128.handle, fake, 0, C.byref(cache), fake, 0, 128, fake, None, 0.1,
