@@ -423,6 +423,8 @@ int32_t wave_attn_splitkv(const wave_plan_t* plan, const void* d_desc, int32_t r
   return ok();
 }
 
+}  // extern "C"
+
 namespace {
 
 int32_t chain_plan_check(const wave::Plan& p, const std::string& f) {
@@ -432,6 +434,8 @@ int32_t chain_plan_check(const wave::Plan& p, const std::string& f) {
 }
 
 }  // namespace
+
+extern "C" {
 
 int32_t qkv_project_workspace(const wave_plan_t* plan, int32_t round, size_t* bytes) {
   if (!plan || !bytes) return set_error(WAVE_ERR_INVALID_ARG, "qkv_project_workspace: null argument");
