@@ -28,6 +28,7 @@ CLEAN, SAME_LEVEL, PROGRESSIVE = WAVE_CLEAN, WAVE_SAME_LEVEL, WAVE_PROGRESSIVE
 SERIAL, WAVE = WAVE_SCHED_SERIAL, WAVE_SCHED_WAVE
 
 __all__ = ["Plan", "KVCache", "wave_plan", "kv_write", "wave_attn", "wave_round", "wave_attn_splitkv",
+           "wave_attn_splitkv_noalloc",
            "attn_workspace", "splitkv_workspace_bytes", "qkv_project", "chain_store", "WaveError",
            "CLEAN", "SAME_LEVEL", "PROGRESSIVE", "SERIAL", "WAVE", "WAVE_LEVEL_COND",
            "WAVE_Q_TILE", "WAVE_KEY_TILE", "WAVE_NODE_UPDATE", "WAVE_NODE_REFRESH"]
@@ -292,6 +293,21 @@ def wave_attn_splitkv(plan: Plan, d_desc, round: int, cache: KVCache, q, scale: 
                                              C.c_void_p(lse.data_ptr() if lse is not None else 0),
                                              float(scale), splits, C.c_void_p(workspace.data_ptr()),
                                              workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
+    return o, lse
+
+
+def wave_attn_splitkv_noalloc(plan: Plan, d_desc, round: int, cache: KVCache, q, scale: float,
+                              num_splits: int = 0, o=None, lse=None, stream=None):
+    """wave_attn_splitkv with its partial results in the library's per-device
+    scratch array (no workspace, no device allocation by the library).  o and
+    lse must be passed in for a call that allocates nothing at all; calls
+    that overlap on one device race on the shared scratch."""
+    o, lse = _attn_outputs(plan, round, cache, q, o, lse, lse is not None or o is None)
+    _lib.check(_lib.load().wave_attn_splitkv_noalloc(plan.handle, C.c_void_p(d_desc.data_ptr()), round,
+                                                     C.byref(cache.c), C.c_void_p(q.data_ptr()), _dtype_code(q),
+                                                     q.stride(0), C.c_void_p(o.data_ptr()),
+                                                     C.c_void_p(lse.data_ptr() if lse is not None else 0),
+                                                     float(scale), int(num_splits), _stream_ptr(stream)))
     return o, lse
 
 

@@ -21,11 +21,12 @@ WAVE_DTYPE_BF16, WAVE_DTYPE_FP32 = 0, 1
 WAVE_LEVEL_COND = -1
 WAVE_Q_TILE = 256
 WAVE_KEY_TILE = 64
+WAVE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 EXPORTS = ("wave_plan", "wave_plan_view_get", "wave_plan_desc_size", "wave_plan_desc_pack",
            "wave_plan_destroy", "kv_write", "wave_attn_workspace", "wave_attn", "wave_attn_splitkv_workspace",
-           "wave_round", "wave_attn_splitkv", "qkv_project_workspace", "qkv_project", "chain_store",
-           "wave_last_error")
+           "wave_round", "wave_attn_splitkv", "wave_attn_splitkv_noalloc", "qkv_project_workspace",
+           "qkv_project", "chain_store", "wave_last_error")
 
 
 class PlanParams(C.Structure):
@@ -114,6 +115,10 @@ def load() -> C.CDLL:
                                       C.c_void_p, C.c_int32, C.c_int64, C.c_void_p, C.c_void_p,
                                       C.c_float, C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p]
     lib.wave_attn_splitkv.restype = C.c_int32
+    lib.wave_attn_splitkv_noalloc.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.POINTER(KvCache),
+                                              C.c_void_p, C.c_int32, C.c_int64, C.c_void_p, C.c_void_p,
+                                              C.c_float, C.c_int32, C.c_void_p]
+    lib.wave_attn_splitkv_noalloc.restype = C.c_int32
     lib.qkv_project_workspace.argtypes = [C.c_void_p, C.c_int32, C.POINTER(C.c_size_t)]
     lib.qkv_project_workspace.restype = C.c_int32
     lib.qkv_project.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.POINTER(KvCache), C.c_void_p, C.c_int32,

@@ -390,37 +390,85 @@ int32_t wave_attn_splitkv_workspace(const wave_plan_t* plan, int32_t round, int3
   return ok();
 }
 
-int32_t wave_attn_splitkv(const wave_plan_t* plan, const void* d_desc, int32_t round, const wave_kv_cache* cache,
-                          const void* q, int32_t q_dtype, int64_t q_row_stride, void* o, float* lse, float scale,
-                          int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
-  wave::AttnArgs a;
-  const int32_t rc = attn_common(plan, d_desc, round, cache, q, q_dtype, q_row_stride, o, lse, scale,
-                                 "wave_attn_splitkv", a);
+}  // extern "C"
+
+namespace {
+
+// Checks of the split-KV calls; fills the launch arguments except the
+// partial-result pointers and returns the workspace the call needs.
+int32_t splitkv_prepare(const wave_plan_t* plan, const void* d_desc, int32_t round, const wave_kv_cache* cache,
+                        const void* q, int32_t q_dtype, int64_t q_row_stride, void* o, float* lse, float scale,
+                        int32_t num_splits, const char* fn, wave::AttnArgs& a, size_t* need, size_t* lse_off) {
+  const int32_t rc = attn_common(plan, d_desc, round, cache, q, q_dtype, q_row_stride, o, lse, scale, fn, a);
   if (rc != WAVE_OK) return rc;
+  const std::string f(fn);
   if (num_splits < 0 || num_splits > 4096)
-    return set_error(WAVE_ERR_INVALID_ARG, "wave_attn_splitkv: num_splits must be in [0, 4096]");
+    return set_error(WAVE_ERR_INVALID_ARG, f + ": num_splits must be in [0, 4096]");
   const wave::Plan& p = plan->p;
   const int32_t s = num_splits == 0 ? auto_splits(p, round, cache->heads, cache->head_dim) : num_splits;
-  size_t lse_off = 0;
-  const size_t need = splitkv_bytes(p, round, cache->heads, cache->head_dim, s, &lse_off);
-  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
-    return set_error(WAVE_ERR_INVALID_ARG, "wave_attn_splitkv: workspace must be non-null and 256-byte aligned");
-  if (workspace_bytes < need)
-    return set_error(WAVE_ERR_CAPACITY, "wave_attn_splitkv: workspace smaller than wave_attn_splitkv_workspace()");
   if (static_cast<int64_t>(a.num_work) * cache->heads * s > INT32_MAX)
-    return set_error(WAVE_ERR_UNSUPPORTED, "wave_attn_splitkv: too many workgroups");
+    return set_error(WAVE_ERR_UNSUPPORTED, f + ": too many workgroups");
+  *need = splitkv_bytes(p, round, cache->heads, cache->head_dim, s, lse_off);
   a.num_splits = s;
   a.part_rows = p.round_q_rows[round];
-  a.part_o = static_cast<float*>(workspace);
-  a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + lse_off);
-  if (s == 1) {
+  return WAVE_OK;
+}
+
+int32_t splitkv_launch(wave::AttnArgs& a, void* scratch, size_t lse_off, void* stream, const char* fn) {
+  if (a.num_splits > 1) {
+    a.part_o = static_cast<float*>(scratch);
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(scratch) + lse_off);
+  } else {
     // one split: the plain kernel writes o and lse directly
     a.part_o = nullptr;
     a.part_lse = nullptr;
   }
   const hipError_t e = wave::launch_wave_attn(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return set_error(WAVE_ERR_HIP, std::string("wave_attn_splitkv: ") + hipGetErrorString(e));
+  if (e != hipSuccess) return set_error(WAVE_ERR_HIP, std::string(fn) + ": " + hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t wave_attn_splitkv(const wave_plan_t* plan, const void* d_desc, int32_t round, const wave_kv_cache* cache,
+                          const void* q, int32_t q_dtype, int64_t q_row_stride, void* o, float* lse, float scale,
+                          int32_t num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  wave::AttnArgs a;
+  size_t need = 0, lse_off = 0;
+  const char* fn = "wave_attn_splitkv";
+  const int32_t rc = splitkv_prepare(plan, d_desc, round, cache, q, q_dtype, q_row_stride, o, lse, scale,
+                                     num_splits, fn, a, &need, &lse_off);
+  if (rc != WAVE_OK) return rc;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+    return set_error(WAVE_ERR_INVALID_ARG, "wave_attn_splitkv: workspace must be non-null and 256-byte aligned");
+  if (workspace_bytes < need)
+    return set_error(WAVE_ERR_CAPACITY, "wave_attn_splitkv: workspace smaller than wave_attn_splitkv_workspace()");
+  return splitkv_launch(a, workspace, lse_off, stream, fn);
+}
+
+int32_t wave_attn_splitkv_noalloc(const wave_plan_t* plan, const void* d_desc, int32_t round,
+                                  const wave_kv_cache* cache, const void* q, int32_t q_dtype, int64_t q_row_stride,
+                                  void* o, float* lse, float scale, int32_t num_splits, void* stream) {
+  static_assert(wave::kScratchBytes == WAVE_NOALLOC_SCRATCH_BYTES, "scratch size: header and library disagree");
+  wave::AttnArgs a;
+  size_t need = 0, lse_off = 0;
+  const char* fn = "wave_attn_splitkv_noalloc";
+  const int32_t rc = splitkv_prepare(plan, d_desc, round, cache, q, q_dtype, q_row_stride, o, lse, scale,
+                                     num_splits, fn, a, &need, &lse_off);
+  if (rc != WAVE_OK) return rc;
+  void* scratch = nullptr;
+  if (a.num_splits > 1) {
+    if (need > wave::kScratchBytes)
+      return set_error(WAVE_ERR_CAPACITY, std::string(fn) + ": the call needs " + std::to_string(need) +
+                                              " bytes of scratch, above WAVE_NOALLOC_SCRATCH_BYTES (" +
+                                              std::to_string(wave::kScratchBytes) +
+                                              "); use fewer splits, or wave_attn_splitkv with a workspace");
+    const hipError_t e = wave::scratch_buffer(&scratch);
+    if (e != hipSuccess) return set_error(WAVE_ERR_HIP, std::string(fn) + ": scratch lookup: " + hipGetErrorString(e));
+  }
+  return splitkv_launch(a, scratch, lse_off, stream, fn);
 }
 
 }  // extern "C"

@@ -94,4 +94,10 @@ hipError_t launch_qkv_project(const ProjArgs& a, hipStream_t stream);
 hipError_t launch_chain_store(const StoreArgs& a, hipStream_t stream);
 hipError_t launch_wave_attn(const AttnArgs& a, hipStream_t stream);
 
+// Size of the per-device scratch array behind the allocation-free split-KV
+// entry point, and the lookup of the current device's copy (its device
+// address, found once per device and kept).
+constexpr size_t kScratchBytes = size_t(32) << 20;
+hipError_t scratch_buffer(void** ptr);
+
 }  // namespace wave

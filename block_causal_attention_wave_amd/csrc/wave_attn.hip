@@ -33,6 +33,8 @@
 // with two waves per SIMD the hardware interleaves them as well.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -722,6 +724,40 @@ constexpr int kWaves = 8;
 constexpr int kQB = kQTile / (32 * kWaves);
 
 }  // namespace
+
+// Scratch of the allocation-free split-KV entry point: partial O and LSE of
+// one call.  Each device holds its own copy for the life of the process; in
+// host code `scratch` names a host-side stand-in, so kernels only ever get
+// the device address that scratch_buffer() looks up.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t scratch_buffer(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // First call on this device (which is current here): look up this
+    // device's copy of the array once and keep its address.
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 hipError_t launch_wave_attn(const AttnArgs& a, hipStream_t stream) {
   if (a.num_work == 0) return hipSuccess;

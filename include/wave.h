@@ -40,7 +40,9 @@
  * All int32 status returns: WAVE_OK or a negative WAVE_ERR_*; the message of
  * the last failure on the calling thread is returned by wave_last_error().
  * No C++ exception crosses this boundary.  The library never allocates or
- * frees device memory: every device buffer belongs to the caller.
+ * frees device memory: every device buffer belongs to the caller, except the
+ * fixed per-device scratch array behind wave_attn_splitkv_noalloc, which
+ * comes with the library's code object.
  */
 #ifndef WAVE_H
 #define WAVE_H
@@ -258,6 +260,26 @@ int32_t wave_attn_splitkv(const wave_plan_t* plan, const void* d_desc, int32_t r
                           int64_t q_row_stride, void* o, float* lse, float scale,
                           int32_t num_splits, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/* Bytes of device scratch behind wave_attn_splitkv_noalloc. */
+#define WAVE_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* wave_attn_splitkv without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The partial results live in a
+ * library-owned array of WAVE_NOALLOC_SCRATCH_BYTES per device, created with
+ * the library's code object on each device and held until the process ends;
+ * this call allocates and frees no device memory.  A call whose split count
+ * needs more than that (wave_attn_splitkv_workspace() bytes) fails with
+ * WAVE_ERR_CAPACITY before any launch; num_splits = 1 needs none.  Every call
+ * on one device shares that device's array and overwrites it: calls that
+ * overlap on one device (different streams, or different threads without
+ * ordering) race and must not be issued.  Results equal wave_attn_splitkv's
+ * with the same split count.  Other arguments as for wave_attn_splitkv. */
+int32_t wave_attn_splitkv_noalloc(const wave_plan_t* plan, const void* d_desc, int32_t round,
+                                  const wave_kv_cache* cache, const void* q, int32_t q_dtype,
+                                  int64_t q_row_stride, void* o, float* lse, float scale,
+                                  int32_t num_splits, void* stream);
 
 /* ---- Toy denoiser chain: the steps on either side of the attention ----
  *

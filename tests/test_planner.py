@@ -231,6 +231,23 @@ def test_device_calls_validate_before_launch():
     assert s.value == 3 and b.value >= 3 * 128 * 2 * 64 * 4 + 3 * 2 * 128 * 4
     assert lib.wave_attn_splitkv_workspace(pn.handle, 9, 2, 64, 3, C.byref(b), C.byref(s)) != 0
 
+    # allocation-free split-KV: a split count whose partials exceed the
+    # library's scratch is refused before any launch; so are bad arguments
+    def noalloc(splits=2, q=fake):
+        return lib.wave_attn_splitkv_noalloc(pn.handle, fake, 0, C.byref(cache), q, 0, 128, fake, None, 0.1,
+                                             splits, stream)
+
+    assert noalloc(q=None) == _lib.WAVE_ERR_INVALID_ARG
+    assert noalloc(splits=-1) == _lib.WAVE_ERR_INVALID_ARG
+    wide = native(3, 2, op.SAME_LEVEL, op.WAVE, -1, 4096, 0)
+    wcache = _lib.KvCache(0x10000, 0x20000, wide.num_phys_slots, 40, 128, wide.lpad())
+    b = C.c_size_t()
+    assert lib.wave_attn_splitkv_workspace(wide.handle, 2, 40, 128, 4, C.byref(b), None) == 0
+    assert b.value > _lib.WAVE_NOALLOC_SCRATCH_BYTES
+    assert lib.wave_attn_splitkv_noalloc(wide.handle, fake, 2, C.byref(wcache), fake, 0, 40 * 128, fake, None,
+                                         0.1, 4, stream) == _lib.WAVE_ERR_CAPACITY
+    assert b"WAVE_NOALLOC_SCRATCH_BYTES" in lib.wave_last_error()
+
     def kvw(round_=0, src=fake, dt=0, stride=128):
         return lib.kv_write(pn.handle, fake, round_, C.byref(cache), src, src, dt, stride, stream)
 
