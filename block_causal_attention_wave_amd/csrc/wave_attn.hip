@@ -30,7 +30,8 @@
 // Each 32-key step issues the next block's scores and the previous block's
 // P.V product on the matrix cores and forms the current block's
 // probabilities on the vector ALUs, interleaved in one instruction stream;
-// with two waves per SIMD the hardware interleaves them as well.
+// with two waves per SIMD the hardware interleaves them as well, and the
+// two waves take turns, tile by tile, at the higher issue priority.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -560,6 +561,14 @@ void wave_attn_kernel(AttnArgs a) {
       constexpr int SP = (ST + NS - 1) % NS;  // stage of tile n-1
       const char* kst = lds + ST * C::KBYTES;
       const char* vst = lds + vregion + ST * C::VBYTES;
+      // Issue priority alternates tile by tile between the two waves that
+      // share a SIMD (waves w and w+4).  At equal priority the older wave
+      // always wins, runs ahead, and then idles at the tile barrier while
+      // the younger one finishes alone without a partner to overlap with.
+      if constexpr (KB == 0) {
+        if (((wv_u >> 2) ^ n) & 1) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+      }
       const int valid = cur.valid();
       const bool has_next = KB == 0 || n + 1 < total_tiles;
       if constexpr (KB == 1) {
@@ -579,19 +588,24 @@ void wave_attn_kernel(AttnArgs a) {
         }
         float bsum[QB];
         softmax_block<QB>(scur, c2, mref, pprev, bsum);
-        // Instruction order of the step: two LDS operand reads ahead, then
-        // (MFMA, 3 VALU, LDS read) groups.
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        // Instruction order of the step: four LDS operand reads ahead, then
+        // groups of (MFMA, one exp2, 2 other VALU, LDS read).  The VALU mask
+        // (0x002) does not take transcendentals; they get their own groups
+        // (0x400), one per MFMA.
+        constexpr int kAhead = 4;
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
   #pragma unroll
-        for (int i = 0; i < 16 - 2; ++i) {
+        for (int i = 0; i < 16 - kAhead; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
   #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < kAhead; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
         }
         settle(bsum, pprev, kst, KB, valid - 32 * KB);
       }
@@ -617,6 +631,7 @@ void wave_attn_kernel(AttnArgs a) {
     // P.V of the last block (block 1 of the last tile).
     if (active) pv_block<HD, QB>(lds + vregion + ((total_tiles - 1) % NS) * C::VBYTES, 1, pprev, o, lane);
 
+    __builtin_amdgcn_s_setprio(0);
     // Epilogue: O = O^T / l, LSE = ln2 * (mref + log2 l).
     if (!active) return;
     const int64_t orow_stride = (int64_t)a.heads * HD;
