@@ -127,6 +127,8 @@ def main():
     ap.add_argument("--chain", action="store_true",
                     help="whole rollouts of the toy denoiser chain (QKV projection into the cache + attention)")
     ap.add_argument("--layers", type=int, default=0, help="rollout layers (0 = the workload's)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="with workload 2, skip the Wan-Streamer round and audio decode timed after it")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -145,7 +147,37 @@ def main():
     if args.rollout:
         rollout_bench(args, device)
         return
-    w = wi.WORKLOADS[args.workload]
+    if args.workload == 3:
+        print("workload 3 is a whole rollout: run it with --rollout", file=sys.stderr)
+        sys.exit(2)
+    out = measure_round(args, device, args.workload, args.steps, args.warmup, cpu=not args.no_cpu_baseline,
+                        copy_calibration=args.copy_calibration)
+    if args.workload == 2 and not args.no_extra:
+        # The Wan-Streamer-shaped round and its audio decode, timed in the same run.
+        extra = {}
+        for key in (5, 6):
+            r = measure_round(args, device, key, max(10, args.steps // 2), max(3, args.warmup // 2), cpu=False,
+                              copy_calibration=False)
+            extra[r["config"]["workload"]] = {
+                "metric": r["roofline"]["unit"], "achieved": r["roofline"]["achieved"],
+                "frac_of_peak": r["roofline"]["frac"], "bound": r["roofline"]["bound"],
+                "attn_ms": r["attn_ms"], "attn_ms_median": r["attn_ms_median"], "round_ms": r["round_ms"],
+                "kv_write_ms": r["kv_write_ms"], "kv_write_gbps": r["kv_write_gbps"],
+                "algorithmic_tflop": r["config"]["algorithmic_tflop"], "attn_compulsory_mb": r["attn_compulsory_mb"],
+                "splitkv_splits": r["config"]["splitkv_splits"], "traffic": r["roofline"]["traffic"],
+                "steps": r["steps"]}
+        out["extra_workloads"] = extra
+    print(json.dumps(out), flush=True)
+
+
+def measure_round(args, device, key, steps, warmup, cpu, copy_calibration):
+    """kv_write + wave_attn of one round of workload `key`, timed over `steps`
+    steps after `warmup`; returns the bench JSON object (without printing it)."""
+    import torch
+    import block_causal_attention_wave_amd as wv
+    import wave_inputs as wi
+
+    w = wi.WORKLOADS[key]
     policy = w.policies[0]
     t_meas = w.round if w.round >= 0 else 16
     layer = 0
@@ -204,12 +236,12 @@ def main():
 
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
+        for _ in range(warmup):
             wv.kv_write(plan, desc, t_meas, cache, k_src, v_src, stream=stream)
             attn(stream)
         torch.cuda.synchronize()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-                torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+                torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for e0, e1, e2 in evs:
@@ -226,7 +258,7 @@ def main():
         eprint("non-finite output: a read outside the written slots")
         sys.exit(3)
 
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = wall * 1e3 / steps
     attn_avg = float(attn_ms.mean())
     achieved = flops / (attn_avg * 1e-3) / 1e12
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -242,7 +274,7 @@ def main():
            f"step {ms_per_step:.3f} ms wall")
 
     copy_ms = None
-    if args.copy_calibration:
+    if copy_calibration:
         n = 1 << 29  # 1 GiB of bf16
         src = torch.ones(n, dtype=torch.bfloat16, device=device)
         dst = torch.empty_like(src)
@@ -256,17 +288,17 @@ def main():
         eprint(f"[bench] 1 GiB copy {copy_ms:.3f} ms = {2 * (1 << 30) / (copy_ms * 1e-3) / 1e9:.0f} GB/s")
         del src, dst
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, plan, t_meas, nodes, policy, layer, device, args.cpu_rows)
+    cpu_res = None
+    if cpu:
+        cpu_res = cpu_baseline(w, plan, t_meas, nodes, policy, layer, device, args.cpu_rows)
 
     out = {
         "metric": "block-causal attn TFLOP/s (% bf16 MFMA peak) + ms/wave round, 832x480, 7 chunks",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -300,22 +332,24 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic_from_profile(args.workload),
+            "traffic": traffic_from_profile(key),
         } if not decode else {
             "bound": "hbm",
             "achieved": round(attn_gbps, 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(attn_gbps / PEAK_HBM_GBPS, 4),
-            "traffic": traffic_from_profile(args.workload),
+            "traffic": traffic_from_profile(key),
         }),
         "attn_compulsory_mb": round(attn_bytes / 1e6, 2),
         "attn_gbps": round(attn_gbps, 1),
-        "cpu_baseline": cpu,
+        "cpu_baseline": cpu_res,
     }
     if copy_ms is not None:
         out["copy_1gib_ms"] = round(copy_ms, 4)
-    print(json.dumps(out), flush=True)
+    del cache, q, o, lse, k_src, v_src, workspace
+    torch.cuda.empty_cache()
+    return out
 
 
 def chain_bench(args, device):
@@ -490,11 +524,15 @@ def cpu_baseline(w, plan, t_meas, nodes, policy, layer, device, rows_per_node):
     import wave_inputs as wi
     from oracle import plan as op
     from oracle.rollout import rollout
+    # The oracle's dense products run on numpy's BLAS thread pool, which takes
+    # the process's CPU share (OMP_NUM_THREADS where it is set, else every CPU
+    # the process may run on); `cores` is that pool's size, the threads used.
+    affinity = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = len(os.sched_getaffinity(0))
+        threads = int(os.environ.get("OMP_NUM_THREADS", affinity))
 
     qlen = w.query_len or w.chunk_len
     p = op.Params(w.B, w.K, policy, op.SERIAL, w.history_cap, w.chunk_len, w.cond_len, w.query_len)
@@ -541,6 +579,7 @@ def cpu_baseline(w, plan, t_meas, nodes, policy, layer, device, rows_per_node):
         "cores": int(threads),
         "kind": "oracle",
         "cpu_model": cpu_model,
+        "affinity_cpus": affinity,
         "sample": f"{len(rows)} query rows of each of the {len(nodes)} nodes of round {t_meas}, "
                   f"all {w.heads} heads, fp64 dense-mask attention over every live slot; "
                   f"{secs:.1f} s wall; full-round estimate {secs * qlen / len(rows):.0f} s",

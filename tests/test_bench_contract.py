@@ -41,3 +41,12 @@ def test_bench_json_line(gpu_device):
     assert rf["traffic"] is None or rf["traffic"] > 0
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"] and cb["unit"]
+    assert cb["affinity_cpus"] >= 1
+    # the Wan-Streamer round (MFMA-bound) and its audio decode (HBM-bound), timed in the same run
+    ex = d["extra_workloads"]
+    assert len(ex) == 2
+    bounds = sorted(v["bound"] for v in ex.values())
+    assert bounds == ["hbm", "mfma"]
+    for v in ex.values():
+        assert v["achieved"] > 0 and 0 < v["frac_of_peak"] < 1 and v["attn_ms"] > 0
+        assert v["metric"] == ("GB/s" if v["bound"] == "hbm" else "TFLOP/s")
