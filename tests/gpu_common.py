@@ -145,13 +145,13 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, what=""):
     return stats
 
 
-def sample_rows(L, n=256, seed=1234, q_tile=256):
+def sample_rows(L, n=256, seed=1234, q_tile=256, ragged=True):
     """Deterministic query-row sample: first/last 8 rows, the whole ragged last
-    q-tile, and random rows up to n."""
+    q-tile (when `ragged`), and random rows up to n."""
     rng = np.random.default_rng(seed)
     must = set(range(min(8, L))) | set(range(max(0, L - 8), L))
     last_tile = (L // q_tile) * q_tile
-    if last_tile < L:
+    if ragged and last_tile < L:
         must |= set(range(last_tile, L))
     rest = [r for r in rng.permutation(L).tolist() if r not in must]
     rows = sorted(must | set(rest[:max(0, n - len(must))]))

@@ -252,54 +252,50 @@ def test_wan13b_steady_round_sampled(gpu_device):
 
 
 def test_streamer_round_sampled(gpu_device):
-    """The 640x368 Wan-Streamer shape (cond 512, 40 heads) round 7, sampled rows, 8 heads."""
+    """The 640x368 Wan-Streamer shape (cond 512, 40 heads) round 7: every head
+    of both nodes on 256 sampled rows (first and last 8, the ragged last query
+    tile, seeded random rows)."""
     w = wi.WORKLOADS[5]
-    log(f"{w.name}: GPU round {w.round}, oracle on sampled rows")
-    heads = list(range(0, 40, 5))
-    got, ref, rows, plan = _device_round(w, wi.SAME_LEVEL, 0, w.round, gpu_device, rows_per_node=192, heads=heads)
+    log(f"{w.name}: GPU round {w.round}, oracle on sampled rows, all {w.heads} heads")
+    got, ref, rows, plan = _device_round(w, wi.SAME_LEVEL, 0, w.round, gpu_device, rows_per_node=256)
     assert len(ref) == 2
     for key, (o_ref, lse_ref) in ref.items():
         o, lse = got[key]
-        s = compare(o[rows][:, heads], lse[heads][:, rows], o_ref[:, heads], lse_ref[heads], f"node {key}")
+        s = compare(o[rows], lse[:, rows], o_ref, lse_ref, f"node {key}")
+        # every head on its own: a head-indexing fault in any one head fails here
+        for h in range(w.heads):
+            compare(o[rows][:, h:h + 1], lse[h:h + 1][:, rows], o_ref[:, h:h + 1], lse_ref[h:h + 1], f"node {key} head {h}")
         log(f"  node {key}: {s}")
 
 
-def test_long_video_capped_history_sampled(gpu_device):
-    """B=28, K=4, history capped at 6 chunks, sigma 0.5: a steady round."""
-    w = wi.WORKLOADS[4]
-    t = 16
-    log(f"{w.name}: GPU round {t}, oracle on sampled rows, 4 heads")
-    heads = [0, 3, 7, 11]
-    got, ref, rows, plan = _device_round(w, wi.PROGRESSIVE, 0, t, gpu_device, rows_per_node=128, heads=heads)
-    assert len(ref) == 5
-    for key, (o_ref, lse_ref) in ref.items():
-        o, lse = got[key]
-        s = compare(o[rows][:, heads], lse[heads][:, rows], o_ref[:, heads], lse_ref[heads], f"node {key}")
-        log(f"  node {key}: {s}")
-
-
-@pytest.mark.parametrize("layer", [0, 14, 29])
-@pytest.mark.parametrize("policy", [wi.CLEAN, wi.SAME_LEVEL, wi.PROGRESSIVE])
-def test_wan13b_k5_rollout_sampled(gpu_device, policy, layer):
-    """The 832x480 seven-chunk K=5 rollouts at full size (one of the 30
-    layers): every round of the pipelined plan on the GPU, with freed slots
-    poisoned, against the oracle's serial rollout on sampled rows of 2 heads,
-    for every node of chunks 0, 3 and 6."""
+def test_long_video_capped_history_every_steady_round(gpu_device):
+    """B=28, K=4, history capped at 6 chunks, sigma 0.5: the whole pipelined
+    rollout on the GPU with freed slots poisoned after every round; every node
+    of every steady round (10-27, when all four levels are in flight and the
+    window is full) against the oracle's serial rollout, all 12 heads, on 24
+    sampled rows per node (first and last 8, and 8 seeded random rows; the
+    ragged last query tile changes from round to round: rows 4608-4679 of
+    round 16's nodes are added)."""
     import torch
-    w = wi.WORKLOADS[3]
-    heads = [0, 7]
-    log(f"{w.name}: policy {policy} layer {layer}, all rounds")
-    plan = wv.wave_plan(B=w.B, K=w.K, policy=policy, sched=wv.WAVE, chunk_len=w.chunk_len)
+    w = wi.WORKLOADS[4]
+    log(f"{w.name}: every round on the GPU, oracle on steady rounds 10-27, all heads")
+    plan = wv.wave_plan(B=w.B, K=w.K, policy=wi.PROGRESSIVE, sched=wv.WAVE, chunk_len=w.chunk_len,
+                        history_cap=w.history_cap)
     desc = plan.upload(gpu_device)
     cache = wv.KVCache(plan.num_phys_slots, w.heads, w.head_dim, plan.lpad(), gpu_device, fill=float("nan"))
     freed = freed_after(plan)
-    rows = sample_rows(w.chunk_len, 96)
-    want = {(n[0], n[1]) for n in plan.nodes.tolist() if n[0] in (0, 3, 6)}
-    host = {}
+    base_rows = sample_rows(w.chunk_len, 24, ragged=False)
+    tail_rows = sample_rows(w.chunk_len, 24 + 72)  # adds the ragged last query tile
+    steady = range(10, 28)
+    want = {(n[0], n[1]) for t in steady for n in plan.round_nodes(t).tolist()}
+    round16 = {(n[0], n[1]) for n in plan.round_nodes(16).tolist()}
+    rows_of = {key: tail_rows if key in round16 else base_rows for key in want}
+    host = {}  # exact bf16 inputs, widened to fp64 when the oracle asks
 
     def dev(c, lv, kind):
-        t = wi.device_tensor(w, layer, c, lv, kind, gpu_device, policy)
-        host[(c, lv, kind)] = t[:, heads].float().cpu().numpy().astype(np.float64)
+        t = wi.device_tensor(w, 0, c, lv, kind, gpu_device, wi.PROGRESSIVE)
+        if kind != "q" or (c, lv) in want:
+            host[(c, lv, kind)] = t.cpu()
         return t
 
     got = {}
@@ -314,24 +310,95 @@ def test_wan13b_k5_rollout_sampled(gpu_device, policy, layer):
         torch.cuda.synchronize()
         for n in nodes:
             if (n[0], n[1]) in want:
-                sel = n[4] + rows
-                got[(n[0], n[1])] = (o[sel][:, heads].float().cpu().numpy(), lse[heads][:, sel].cpu().numpy())
+                sel = n[4] + rows_of[(n[0], n[1])]
+                got[(n[0], n[1])] = (o[sel].float().cpu().numpy(), lse[:, sel].cpu().numpy())
         del k_src, v_src, q, o, lse
         poison_slots(cache, freed[t])
 
+    def f64(x):
+        return x.float().numpy().astype(np.float64)
+
     class DevInputs:
         def q64(self, c, lv):
-            return host[(c, lv, "q")]
+            return f64(host[(c, lv, "q")])
 
         def kv64(self, c, lv):
-            return host[(c, lv, "k")], host[(c, lv, "v")]
+            return f64(host[(c, lv, "k")]), f64(host[(c, lv, "v")])
+
+    ref = oracle_rollout(w.B, w.K, wi.PROGRESSIVE, w.history_cap, w.chunk_len, 0, DevInputs(), w.scale,
+                         rows=lambda c, lv: rows_of[(c, lv)], want=want)
+    assert set(ref) == want == set(got) and len(want) == 18 * 5
+    worst = 0.0
+    for key in sorted(want):
+        s = compare(got[key][0], got[key][1], ref[key][0], ref[key][1], f"node {key}")
+        for h in range(w.heads):
+            compare(got[key][0][:, h:h + 1], got[key][1][h:h + 1], ref[key][0][:, h:h + 1], ref[key][1][h:h + 1],
+                    f"node {key} head {h}")
+        worst = max(worst, s["rel_fro"])
+    log(f"  {len(want)} nodes of rounds 10-27, all heads; worst relative Frobenius {worst:.2e}")
+
+
+@pytest.mark.parametrize("layer", [0, 14, 29])
+@pytest.mark.parametrize("policy", [wi.CLEAN, wi.SAME_LEVEL, wi.PROGRESSIVE])
+def test_wan13b_k5_rollout_sampled(gpu_device, policy, layer):
+    """The 832x480 seven-chunk K=5 rollouts at full size (one of the 30
+    layers): every round of the pipelined plan on the GPU, with freed slots
+    poisoned, against the oracle's serial rollout -- every node, all 12
+    heads, 96 sampled rows per node (first and last 8, the ragged last query
+    tile, seeded random rows)."""
+    import torch
+    w = wi.WORKLOADS[3]
+    log(f"{w.name}: policy {policy} layer {layer}, all rounds, every node, all heads")
+    plan = wv.wave_plan(B=w.B, K=w.K, policy=policy, sched=wv.WAVE, chunk_len=w.chunk_len)
+    desc = plan.upload(gpu_device)
+    cache = wv.KVCache(plan.num_phys_slots, w.heads, w.head_dim, plan.lpad(), gpu_device, fill=float("nan"))
+    freed = freed_after(plan)
+    rows = sample_rows(w.chunk_len, 96)
+    want = {(n[0], n[1]) for n in plan.nodes.tolist()}
+    host = {}  # exact bf16 inputs, widened to fp64 when the oracle asks
+
+    def dev(c, lv, kind):
+        t = wi.device_tensor(w, layer, c, lv, kind, gpu_device, policy)
+        host[(c, lv, kind)] = t.cpu()
+        return t
+
+    got = {}
+    for t in range(plan.num_rounds):
+        ws = plan.round_writes(t).tolist()
+        k_src = torch.cat([dev(c, lv, "k") for (c, lv, _, _) in ws])
+        v_src = torch.cat([dev(c, lv, "v") for (c, lv, _, _) in ws])
+        wv.kv_write(plan, desc, t, cache, k_src, v_src)
+        nodes = plan.round_nodes(t).tolist()
+        q = torch.cat([dev(n[0], n[1], "q") for n in nodes])
+        o, lse = wv.wave_attn(plan, desc, t, cache, q, w.scale)
+        torch.cuda.synchronize()
+        for n in nodes:
+            sel = n[4] + rows
+            got[(n[0], n[1])] = (o[sel].float().cpu().numpy(), lse[:, sel].cpu().numpy())
+        del k_src, v_src, q, o, lse
+        poison_slots(cache, freed[t])
+
+    def f64(x):
+        return x.float().numpy().astype(np.float64)
+
+    class DevInputs:
+        def q64(self, c, lv):
+            return f64(host[(c, lv, "q")])
+
+        def kv64(self, c, lv):
+            return f64(host[(c, lv, "k")]), f64(host[(c, lv, "v")])
 
     ref = oracle_rollout(w.B, w.K, policy, -1, w.chunk_len, 0, DevInputs(), w.scale, rows=lambda c, lv: rows,
                          want=want)
     assert set(ref) == want == set(got)
+    worst = 0.0
     for key in sorted(want):
         s = compare(got[key][0], got[key][1], ref[key][0], ref[key][1], f"node {key}")
-    log(f"  {len(want)} nodes; last {s}")
+        for h in range(w.heads):
+            compare(got[key][0][:, h:h + 1], got[key][1][h:h + 1], ref[key][0][:, h:h + 1], ref[key][1][h:h + 1],
+                    f"node {key} head {h}")
+        worst = max(worst, s["rel_fro"])
+    log(f"  {len(want)} nodes, all heads; worst relative Frobenius {worst:.2e}")
 
 
 @pytest.mark.parametrize("balance", [True, False])
@@ -404,11 +471,11 @@ def test_splitkv_grid_parity(gpu_device, policy, H, cond, L, qlen, heads, hd, sp
 
 def test_streamer_audio_decode_splitkv(gpu_device):
     """Decode-shaped Wan-Streamer round: the 64 audio rows of each chunk in round 7
-    (U(6,1) over 23,352 keys, U(7,2) over 26,688 keys) with split-KV, 8 heads
-    checked, against the oracle and against the unsplit kernel."""
+    (U(6,1) over 23,352 keys, U(7,2) over 26,688 keys) with split-KV, all 40
+    heads, against the oracle and against the unsplit kernel."""
     import torch
     w = wi.WORKLOADS[5]
-    qlen, t_meas, heads = 64, 7, list(range(0, 40, 5))
+    qlen, t_meas, heads = 64, 7, list(range(40))
     log(f"{w.name}: audio decode round {t_meas}, split-KV")
     plan = wv.wave_plan(B=w.B, K=w.K, policy=wi.SAME_LEVEL, sched=wv.WAVE, chunk_len=w.chunk_len,
                         cond_len=w.cond_len, query_len=qlen)
@@ -454,6 +521,9 @@ def test_streamer_audio_decode_splitkv(gpu_device):
         a, b = n[4], n[4] + n[5]
         s = compare(o_s[a:b][:, heads], lse_s[heads][:, a:b], ref[key][0][:, heads], ref[key][1][heads],
                     f"node {key}")
+        for h in heads:
+            compare(o_s[a:b][:, h:h + 1], lse_s[h:h + 1][:, a:b], ref[key][0][:, h:h + 1], ref[key][1][h:h + 1],
+                    f"node {key} head {h}")
         log(f"  node {key}: {s}")
 
 
