@@ -179,6 +179,72 @@ def test_chain_matches_oracle(gpu_device, policy, B, K, L, heads, hd, layers):
 CHAIN_REL_FRO = 6e-2
 
 
+# Bound for one stage (projection, then attention) on exact inputs, relative
+# Frobenius norm per node and layer.  Both sides round O to bf16 (unit
+# roundoff u = 2^-8: 8 significand bits), the kernel from its fp32 result and
+# the oracle from fp64.  The two roundings agree except where the pre-rounding
+# values straddle a rounding boundary, and then differ by one bf16 step
+# (2^-8 to 2^-7 relative).  The kernel's pre-rounding error is about
+# d = 1e-3 relative (bf16 P, fp32 sums), so a fraction of about d / 2^-8 =
+# 0.26 of the elements straddle: sqrt(0.26) * 2^-7.5 = 2.8e-3 in RMS, with d
+# in quadrature about 3.0e-3.  Q, K and V are rounded to bf16 from an fp32 sum
+# on the GPU and an fp64 sum in the oracle; the few elements that land one
+# step apart add well under 1e-3.  Bound: 4e-3 (measured worst 2.9e-3).
+STAGE_REL_FRO = 4e-3
+
+
+@pytest.mark.parametrize("policy,B,K,L,heads,hd,layers", CHAIN_GRID)
+def test_chain_each_stage_matches_oracle(gpu_device, policy, B, K, L, heads, hd, layers):
+    """One stage at a time: every round and layer of the chain runs on the GPU
+    (qkv_project into the layer's cache, then wave_attn) with the oracle's own
+    input rows for that layer (the noise, or the oracle's output of the
+    previous layer or of the chunk's previous node), so each output carries
+    the error of a single stage and is held to the one-stage bound instead of
+    the compounded whole-chain bound."""
+    import torch
+    noise, weights = _inputs(40 + L, B, L, heads, hd, layers)
+    scale = 1.0 / math.sqrt(hd)
+    D = heads * hd
+    p = op.Params(B, K, policy, op.SERIAL, -1, L, 0, 0)
+    ref = oc.chain_rollout(p, op.oracle_plan(p), layers, heads, hd, lambda c: noise[c].astype(np.float64),
+                           lambda l: weights[l].astype(np.float64), scale)
+    plan = wv.wave_plan(B=B, K=K, policy=policy, sched=wv.WAVE, chunk_len=L)
+    log(f"chain stages policy={policy} B={B} K={K} L={L} heads={heads} hd={hd} layers={layers}")
+    # the oracle's input rows of every node at every layer
+    prev = {}
+    for n in plan.nodes.tolist():  # nodes in round order; a chunk's nodes in execution order
+        prev[(n[0], n[1])] = prev.get(("last", n[0]))
+        prev[("last", n[0])] = (n[0], n[1])
+
+    def a_in(key, layer):
+        if layer > 0:
+            return ref[key][1][layer - 1].reshape(L, D)
+        return noise[key[0]] if prev[key] is None else ref[prev[key]][0]
+
+    desc = plan.upload(gpu_device)
+    caches = [wv.KVCache(plan.num_phys_slots, heads, hd, plan.lpad(), gpu_device, fill=float("nan"))
+              for _ in range(layers)]
+    w_dev = [torch.from_numpy(w).to(device=gpu_device, dtype=torch.bfloat16) for w in weights]
+    worst = 0.0
+    for t in range(plan.num_rounds):
+        nodes = plan.round_nodes(t).tolist()
+        for layer in range(layers):
+            x = np.concatenate([a_in((n[0], n[1]), layer) for n in nodes]).astype(np.float32)
+            x = torch.from_numpy(x).to(device=gpu_device, dtype=torch.bfloat16)
+            q = wv.qkv_project(plan, desc, t, caches[layer], x, w_dev[layer], x_layout=wv.X_ROUND)
+            o, _ = wv.wave_attn(plan, desc, t, caches[layer], q, scale, balance=False)
+            torch.cuda.synchronize()
+            o = o.float().cpu().numpy()
+            for n in nodes:
+                g = o[n[4]:n[4] + n[5]]
+                r = ref[(n[0], n[1])][1][layer]
+                rel = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30))
+                worst = max(worst, rel)
+                assert np.isfinite(g).all()
+                assert rel <= STAGE_REL_FRO, f"round {t} node {(n[0], n[1])} layer {layer}: rel {rel}"
+    log(f"  worst one-stage relative Frobenius error {worst:.3g}")
+
+
 @pytest.mark.parametrize("policy", [wi.CLEAN, wi.SAME_LEVEL, wi.PROGRESSIVE])
 def test_chain_serial_equals_wave_bitwise(gpu_device, policy):
     """Real data flow through the schedule: serial and pipelined rounds give
