@@ -126,6 +126,9 @@ def main():
     ap.add_argument("--rollout", action="store_true")
     ap.add_argument("--chain", action="store_true",
                     help="whole rollouts of the toy denoiser chain (QKV projection into the cache + attention)")
+    ap.add_argument("--proj", action="store_true",
+                    help="qkv_project against the plain bf16 product (torch.matmul) of the same shape, "
+                         "one round per node count of the Wan2.1-1.3B pipelined plan")
     ap.add_argument("--layers", type=int, default=0, help="rollout layers (0 = the workload's)")
     ap.add_argument("--no-extra", action="store_true",
                     help="with workload 2, skip the Wan-Streamer round and audio decode timed after it")
@@ -143,6 +146,9 @@ def main():
     device = torch.device("cuda:0")
     if args.chain:
         chain_bench(args, device)
+        return
+    if args.proj:
+        proj_bench(args, device)
         return
     if args.rollout:
         rollout_bench(args, device)
@@ -438,6 +444,73 @@ def chain_bench(args, device):
                       "workload": w.name + "-toy-chain", "unit": "ms", "n_gpus": 1, "dtype": "bf16",
                       "data": "synthetic", "timing": "sum of per-(round, layer) qkv_project + wave_attn and "
                       "per-round chain_store event times", "results": results}), flush=True)
+
+
+def proj_bench(args, device):
+    """qkv_project (RMS scaling, Q out, K/V^T into the node's cache slot) and
+    the plain product x @ W^T of the same shape through torch.matmul, on the
+    same box in one run: one round per distinct node count of the Wan2.1-1.3B
+    progressive plan, alternating the two, timed with events."""
+    import torch
+    import block_causal_attention_wave_amd as wv
+    import wave_inputs as wi
+    w = wi.WORKLOADS[3]
+    D = w.heads * w.head_dim
+    plan = wv.wave_plan(B=w.B, K=w.K, policy=wi.PROGRESSIVE, sched=wv.WAVE, chunk_len=w.chunk_len,
+                        history_cap=w.history_cap)
+    desc = plan.upload(device)
+    cache = wv.KVCache(plan.num_phys_slots, w.heads, w.head_dim, plan.lpad(), device, fill=0.0)
+    weight = wi.device_chain_weight(w.key, 0, D, device)
+    weight_t = weight.t().contiguous()  # [D, 3D] for the plain product
+    by_count = {}
+    for t in range(plan.num_rounds):
+        by_count.setdefault(len(plan.round_nodes(t)), t)
+    max_rows = int(plan.round_q_rows.max())
+    x_all = wi.device_normal_bf16(wi.chain_noise_seed(w.key, 0), (max_rows, D), 1.0, device)
+    q = torch.empty((max_rows, w.heads, w.head_dim), dtype=torch.bfloat16, device=device)
+    y = torch.empty((max_rows, 3 * D), dtype=torch.bfloat16, device=device)
+    ws = torch.empty(max_rows * 4 + 256, dtype=torch.uint8, device=device)
+    stream = torch.cuda.Stream()
+    reps, warm = max(args.steps // 5, 5), 3
+    results = []
+    with torch.cuda.stream(stream):
+        for count, t in sorted(by_count.items()):
+            rows = int(plan.round_q_rows[t])
+            x = x_all[:rows]
+            flops = 2.0 * rows * D * 3 * D
+
+            def proj():
+                wv.qkv_project(plan, desc, t, cache, x, weight, q=q[:rows], x_layout=wv.X_ROUND, workspace=ws,
+                               stream=stream)
+
+            def plain():
+                torch.matmul(x, weight_t, out=y[:rows])
+
+            for _ in range(warm):
+                proj()
+                plain()
+            times = {"qkv_project": [], "torch.matmul": []}
+            for r in range(reps):
+                for name, fn in (("qkv_project", proj), ("torch.matmul", plain)):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    fn()
+                    e1.record(stream)
+                    e1.synchronize()
+                    times[name].append(e0.elapsed_time(e1))
+            res = {"nodes": count, "round": t, "rows": rows, "gflop": round(flops / 1e9, 2)}
+            for name, ts in times.items():
+                med = float(np.median(ts))
+                res[name + "_ms"] = round(med, 4)
+                res[name + "_tflops"] = round(flops / (med * 1e-3) / 1e12, 1)
+            eprint(f"[proj] {count} nodes, {rows} rows: qkv_project {res['qkv_project_ms']:.4f} ms = "
+                   f"{res['qkv_project_tflops']:.0f} TFLOP/s; torch.matmul {res['torch.matmul_ms']:.4f} ms = "
+                   f"{res['torch.matmul_tflops']:.0f} TFLOP/s")
+            results.append(res)
+    print(json.dumps({"metric": "qkv_project TFLOP/s against the plain product of the same shape",
+                      "workload": w.name + "-qkv-projection", "unit": "TFLOP/s", "n_gpus": 1, "dtype": "bf16",
+                      "data": "synthetic", "timing": "median of per-call event times, the two alternating",
+                      "results": results}), flush=True)
 
 
 def rollout_bench(args, device):

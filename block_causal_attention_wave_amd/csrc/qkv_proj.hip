@@ -385,9 +385,17 @@ __global__ __launch_bounds__(THREADS, 1) void qkv_gemm_wide_kernel(ProjArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+  // Q and K tiles are multiplied transposed (W rows as the MFMA's A operand,
+  // token rows as B), so that each lane ends with 4 consecutive columns of
+  // one token and the row-major staging below takes 8-byte writes; V tiles
+  // keep tokens consecutive in a lane for the column-major (V^T) staging.
+  const int part = c0 / D;  // 0: Q, 1: K, 2: V (D is a multiple of TN)
+
   // Two stages: after the barrier of k-step ks every wave is done with ks-1,
   // whose stage receives ks+1 while ks is multiplied.
   const int nk = D / TK;
+  auto kloop = [&](auto tr_tag) __attribute__((always_inline)) {
+  constexpr bool TR = decltype(tr_tag)::value;
   issue(0, 0);
   int stage = 0;
   for (int ks = 0; ks < nk; ++ks) {
@@ -417,7 +425,8 @@ __global__ __launch_bounds__(THREADS, 1) void qkv_gemm_wide_kernel(ProjArgs a) {
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][i], bf[s & 1][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = TR ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[s & 1][j], af[s & 1][i], acc[i][j], 0, 0, 0)
+                         : __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][i], bf[s & 1][j], acc[i][j], 0, 0, 0);
     }
     // Keep that order: reads of substeps 0 and 1, then (MFMAs of s, reads of s+2).
     __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
@@ -429,11 +438,31 @@ __global__ __launch_bounds__(THREADS, 1) void qkv_gemm_wide_kernel(ProjArgs a) {
     __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
     stage ^= 1;
   }
+  };
+  if (part == 2) kloop(std::false_type{});
+  else kloop(std::true_type{});
   barrier();  // the epilogue reuses the stages
 
-  // Epilogue as in qkv_gemm_kernel: scale by 1/rms, round, stage in LDS
-  // (column-major for V), then 16-byte stores to Q, K or V^T.
-  const int part = c0 / D;  // 0: Q, 1: K, 2: V (D is a multiple of TN)
+  // Epilogue: scale by 1/rms, round, stage in LDS (column-major for V), then
+  // 16-byte stores to Q, K or V^T.  Q/K lanes hold token (lane & 31) of each
+  // 32-token block and 4 consecutive columns per register quad.
+  if (part != 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wr * 128 + i * 32 + (lane & 31);
+      const float sc = r0 + row < L ? a.row_scale[q_offset + r0 + row] : 0.0f;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = wc * 64 + j * 32 + 8 * g + 4 * (lane >> 5);
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[i][j][4 * g + e] * sc);
+          *reinterpret_cast<bf16x4*>(lds + row * OUT_PITCH_R + col * 2) = v;
+        }
+    }
+  } else {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -448,18 +477,13 @@ __global__ __launch_bounds__(THREADS, 1) void qkv_gemm_wide_kernel(ProjArgs a) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int col = wc * 64 + j * 32 + (lane & 31);
-        if (part == 2) {
-          bf16x4 v;
+        bf16x4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[i][j][4 * g + e] * sc[e]);
-          *reinterpret_cast<bf16x4*>(lds + col * OUT_PITCH_C + row0 * 2) = v;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            *reinterpret_cast<__bf16*>(lds + (row0 + e) * OUT_PITCH_R + col * 2) = (__bf16)(acc[i][j][4 * g + e] * sc[e]);
-        }
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(acc[i][j][4 * g + e] * sc[e]);
+        *reinterpret_cast<bf16x4*>(lds + col * OUT_PITCH_C + row0 * 2) = v;
       }
     }
+  }
   }
   __syncthreads();
   const int heads = a.heads, lpad = a.lpad;
