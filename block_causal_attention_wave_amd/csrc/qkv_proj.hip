@@ -390,6 +390,14 @@ __global__ __launch_bounds__(THREADS, 1) void qkv_gemm_wide_kernel(ProjArgs a) {
   // one token and the row-major staging below takes 8-byte writes; V tiles
   // keep tokens consecutive in a lane for the column-major (V^T) staging.
   const int part = c0 / D;  // 0: Q, 1: K, 2: V (D is a multiple of TN)
+  // 1/rms of token (lane & 31) of each of the wave's 32-token blocks (0 past
+  // the chunk's tokens), fetched now so that the epilogue does not wait.
+  float rsc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = r0 + wr * 128 + i * 32 + (lane & 31);
+    rsc[i] = r < L ? a.row_scale[q_offset + r] : 0.0f;
+  }
 
   // Two stages: after the barrier of k-step ks every wave is done with ks-1,
   // whose stage receives ks+1 while ks is multiplied.
@@ -450,7 +458,7 @@ __global__ __launch_bounds__(THREADS, 1) void qkv_gemm_wide_kernel(ProjArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = wr * 128 + i * 32 + (lane & 31);
-      const float sc = r0 + row < L ? a.row_scale[q_offset + r0 + row] : 0.0f;
+      const float sc = rsc[i];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -470,10 +478,7 @@ __global__ __launch_bounds__(THREADS, 1) void qkv_gemm_wide_kernel(ProjArgs a) {
       const int row0 = wr * 128 + i * 32 + 8 * g + 4 * (lane >> 5);
       float sc[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = r0 + row0 + e;
-        sc[e] = r < L ? a.row_scale[q_offset + r] : 0.0f;
-      }
+      for (int e = 0; e < 4; ++e) sc[e] = __shfl(rsc[i], 8 * g + 4 * (lane >> 5) + e, 64);  // lane t: token t
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int col = wc * 64 + j * 32 + (lane & 31);
