@@ -313,34 +313,48 @@ __global__ __launch_bounds__(THREADS, 1) void qkv_gemm_wide_kernel(ProjArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wv >> 2, wc = wv & 3;  // this wave's 128x64 block of the tile
   // Tile order as in qkv_gemm_kernel: contiguous tile ranges per XCD, groups
-  // of 4 row tiles x all column tiles inside a node.
-  int b = blockIdx.x;
-  {
-    const int per_xcd = (int)(gridDim.x / 8);
-    if (b < per_xcd * 8) b = (b % 8) * per_xcd + b / 8;
-  }
-  const int per_node = a.row_tiles * a.col_tiles;
-  const int node = a.node_begin + b / per_node;
-  int rt, ct;
-  {
+  // of 4 row tiles x all column tiles inside a node.  When a node's last row
+  // tile holds at most 128 rows of the slot (lpad), those tiles, whose
+  // second half of waves skips the arithmetic, go last: they fill the
+  // dispatch's final, part-empty wave at about half the cost of a full tile.
+  const int last_rows = a.lpad - (a.row_tiles - 1) * TM;
+  const int tail = a.row_tiles > 1 && last_rows <= TM / 2 ? 1 : 0;
+  const int body_rows = a.row_tiles - tail;
+  const int body = a.num_nodes * body_rows * a.col_tiles;
+  auto xcd_order = [](int b, int n) {  // workgroup b of n -> tile index, one contiguous range per XCD
+    const int per_xcd = n / 8;
+    return b < per_xcd * 8 ? (b % 8) * per_xcd + b / 8 : b;
+  };
+  int node, rt, ct;
+  if ((int)blockIdx.x < body) {
+    const int b = xcd_order(blockIdx.x, body);
+    const int per_node = body_rows * a.col_tiles;
+    node = a.node_begin + b / per_node;
     constexpr int G = 4;
     const int r = b % per_node;
-    const int full = a.row_tiles / G;
+    const int full = body_rows / G;
     const int gsz = G * a.col_tiles;
     if (r < full * gsz) {
       ct = (r % gsz) / G;
       rt = (r / gsz) * G + r % G;
     } else {
-      const int rem = a.row_tiles - full * G, rr = r - full * gsz;
+      const int rem = body_rows - full * G, rr = r - full * gsz;
       ct = rr / rem;
       rt = full * G + rr % rem;
     }
+  } else {
+    const int b = xcd_order((int)blockIdx.x - body, (int)gridDim.x - body);
+    node = a.node_begin + b / a.col_tiles;
+    ct = b % a.col_tiles;
+    rt = a.row_tiles - 1;
   }
   const int32_t* nd = a.nodes + kDescNodeWords * node;
   const int q_offset = nd[0], L = nd[1], chunk = nd[4];
   const int phys = a.ctx[2 * (nd[2] + nd[3] - 1)];  // the node's own slot: last in its gather list
   const int D = a.model_dim;
   const int r0 = rt * TM, c0 = ct * TN;
+  // waves whose 128 rows all lie past the slot's end only help load and sync
+  const bool active = r0 + wr * 128 < a.lpad;
 
   const char* abase = static_cast<const char*>(a.x) +
                       ((a.x_chunk ? (int64_t)chunk * a.chunk_rows : (int64_t)q_offset) * D) * 2;
@@ -410,40 +424,42 @@ __global__ __launch_bounds__(THREADS, 1) void qkv_gemm_wide_kernel(ProjArgs a) {
     __builtin_amdgcn_s_waitcnt(kWaitExp);  // this thread's loads of k-step ks have landed
     barrier();
     if (ks + 1 < nk) issue(ks + 1, stage ^ 1);
-    const char* sa = lds + stage * STAGE_BYTES;
-    const char* sw = sa + A_BYTES;
-    auto frags = [&](int s, bf16x8 (&af)[4], bf16x8 (&bf)[2]) __attribute__((always_inline)) {
+    if (active) {
+      const char* sa = lds + stage * STAGE_BYTES;
+      const char* sw = sa + A_BYTES;
+      auto frags = [&](int s, bf16x8 (&af)[4], bf16x8 (&bf)[2]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wr * 128 + i * 32 + (lane & 31);
-        af[i] = *reinterpret_cast<const bf16x8*>(sa + row * ROW_BYTES + (((2 * s + (lane >> 5)) ^ swz(row)) * 16));
+        for (int i = 0; i < 4; ++i) {
+          const int row = wr * 128 + i * 32 + (lane & 31);
+          af[i] = *reinterpret_cast<const bf16x8*>(sa + row * ROW_BYTES + (((2 * s + (lane >> 5)) ^ swz(row)) * 16));
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int row = wc * 64 + j * 32 + (lane & 31);
+          bf[j] = *reinterpret_cast<const bf16x8*>(sw + row * ROW_BYTES + (((2 * s + (lane >> 5)) ^ swz(row)) * 16));
+        }
+      };
+      bf16x8 af[2][4], bf[2][2];
+      frags(0, af[0], bf[0]);
+#pragma unroll
+      for (int s = 0; s < TK / 16; ++s) {
+        if (s + 1 < TK / 16) frags(s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = TR ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[s & 1][j], af[s & 1][i], acc[i][j], 0, 0, 0)
+                           : __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][i], bf[s & 1][j], acc[i][j], 0, 0, 0);
       }
+      // Keep that order: reads of substeps 0 and 1, then (MFMAs of s, reads of s+2).
+      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int row = wc * 64 + j * 32 + (lane & 31);
-        bf[j] = *reinterpret_cast<const bf16x8*>(sw + row * ROW_BYTES + (((2 * s + (lane >> 5)) ^ swz(row)) * 16));
+      for (int s = 0; s < TK / 16 - 2; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
       }
-    };
-    bf16x8 af[2][4], bf[2][2];
-    frags(0, af[0], bf[0]);
-#pragma unroll
-    for (int s = 0; s < TK / 16; ++s) {
-      if (s + 1 < TK / 16) frags(s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = TR ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[s & 1][j], af[s & 1][i], acc[i][j], 0, 0, 0)
-                         : __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][i], bf[s & 1][j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
     }
-    // Keep that order: reads of substeps 0 and 1, then (MFMAs of s, reads of s+2).
-    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
-#pragma unroll
-    for (int s = 0; s < TK / 16 - 2; ++s) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
     stage ^= 1;
   }
   };
@@ -454,7 +470,9 @@ __global__ __launch_bounds__(THREADS, 1) void qkv_gemm_wide_kernel(ProjArgs a) {
   // Epilogue: scale by 1/rms, round, stage in LDS (column-major for V), then
   // 16-byte stores to Q, K or V^T.  Q/K lanes hold token (lane & 31) of each
   // 32-token block and 4 consecutive columns per register quad.
-  if (part != 2) {
+  if (!active) {
+    // rows past the slot's end: never written out
+  } else if (part != 2) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = wr * 128 + i * 32 + (lane & 31);
