@@ -509,28 +509,39 @@ __global__ __launch_bounds__(THREADS, 1) void qkv_gemm_wide_kernel(ProjArgs a) {
   }
   }
   __syncthreads();
+  // Write-out: every thread's 16 LDS reads first, then its 16-byte stores.
   const int heads = a.heads, lpad = a.lpad;
-  for (int id = tid; id < TM * (TN / 8); id += THREADS) {
-    if (part == 2) {
-      const int col = id / (TM / 8), tok = r0 + (id % (TM / 8)) * 8;
-      if (tok >= lpad) continue;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + col * OUT_PITCH_C + (tok - r0) * 2);
+  constexpr int ITER = TM * (TN / 8) / THREADS;
+  static_assert(ITER * THREADS == TM * (TN / 8), "whole write-out passes");
+  u32x4 out[ITER];
+  if (part == 2) {
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int id = tid + it * THREADS, col = id / (TM / 8), t8 = (id % (TM / 8)) * 8;
+      out[it] = *reinterpret_cast<const u32x4*>(lds + col * OUT_PITCH_C + t8 * 2);
+    }
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int id = tid + it * THREADS, col = id / (TM / 8), tok = r0 + (id % (TM / 8)) * 8;
       const int h = (c0 - 2 * D + col) / HD, dd = (c0 - 2 * D + col) % HD;
-      __bf16* dst = static_cast<__bf16*>(a.vt) + (((int64_t)phys * heads + h) * HD + dd) * lpad + tok;
-      *reinterpret_cast<u32x4*>(dst) = v;
-    } else {
-      const int row = id / (TN / 8), cc = (id % (TN / 8)) * 8;
-      const int r = r0 + row;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * OUT_PITCH_R + cc * 2);
+      if (tok < lpad)
+        *reinterpret_cast<u32x4*>(static_cast<__bf16*>(a.vt) + (((int64_t)phys * heads + h) * HD + dd) * lpad + tok) =
+            out[it];
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int id = tid + it * THREADS, row = id / (TN / 8), cc = (id % (TN / 8)) * 8;
+      out[it] = *reinterpret_cast<const u32x4*>(lds + row * OUT_PITCH_R + cc * 2);
+    }
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int id = tid + it * THREADS, r = r0 + id / (TN / 8), cc = (id % (TN / 8)) * 8;
       if (part == 0) {
-        if (r >= L) continue;
-        __bf16* dst = static_cast<__bf16*>(a.q) + (int64_t)(q_offset + r) * D + c0 + cc;
-        *reinterpret_cast<u32x4*>(dst) = v;
-      } else {
-        if (r >= lpad) continue;
+        if (r < L) *reinterpret_cast<u32x4*>(static_cast<__bf16*>(a.q) + (int64_t)(q_offset + r) * D + c0 + cc) = out[it];
+      } else if (r < lpad) {
         const int h = (c0 - D + cc) / HD, dd = (c0 - D + cc) % HD;
-        __bf16* dst = static_cast<__bf16*>(a.k) + (((int64_t)phys * heads + h) * lpad + r) * HD + dd;
-        *reinterpret_cast<u32x4*>(dst) = v;
+        *reinterpret_cast<u32x4*>(static_cast<__bf16*>(a.k) + (((int64_t)phys * heads + h) * lpad + r) * HD + dd) = out[it];
       }
     }
   }
