@@ -102,6 +102,11 @@ int32_t kv_prepare(const wave_plan_t* plan, const void* d_desc, int32_t round, c
   a.v_src = v_src;
   a.src_fp32 = src_dtype == WAVE_DTYPE_FP32;
   a.src_row_stride = src_row_stride;
+  // Decode-shaped plans (queries shorter than the chunk): the round's
+  // attention streams the whole history from HBM, so the fresh K/V go out
+  // with non-temporal stores instead of sitting dirty in the last-level
+  // cache, whose write-back would then compete with those reads.
+  a.stream_out = p.params.query_len > 0 && p.params.query_len < p.params.chunk_len;
   return WAVE_OK;
 }
 

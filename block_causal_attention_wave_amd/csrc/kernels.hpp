@@ -24,6 +24,7 @@ struct KvWriteArgs {
   const void* v_src;
   int32_t src_fp32;
   int64_t src_row_stride;  // elements
+  int32_t stream_out;      // non-temporal cache stores (see launch_kv_write)
 };
 
 // One round's attention.  Table pointers are the descriptor's node, ctx and

@@ -9,12 +9,15 @@
 // emits).  The cache keeps, per slot and head, K token-major [lpad][d] and V
 // transposed [d][lpad]; tokens [len, lpad) are zeroed so that a full key tile
 // read past the slot's end multiplies zeros.  fp32 sources are rounded to
-// bf16 to nearest even.  Pure data movement: HBM-bound.
+// bf16 to nearest even.  Pure data movement: HBM-bound.  With stream_out the
+// cache stores are non-temporal (decode-shaped rounds; see abi.cpp).
 //
 // Grid: (lpad / 64 token tiles, writes, heads); 256 threads; one block moves
 // 64 tokens x d of one head of one slot.  V goes through LDS for the
 // transpose; every global access is a 16-byte vector.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "kernels.hpp"
 
@@ -41,7 +44,13 @@ __device__ inline bf16x8 load8(const void* base, int64_t elem) {
   }
 }
 
-template <int HD, bool FP32>
+template <bool NT>
+__device__ inline void store16(__bf16* dst, bf16x8 v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<bf16x8*>(dst));
+  else *reinterpret_cast<bf16x8*>(dst) = v;
+}
+
+template <int HD, bool FP32, bool NT>
 __global__ __launch_bounds__(kThreads) void kv_write_kernel(KvWriteArgs a) {
   constexpr int CH = HD / 8;        // 16-byte chunks per token row
   constexpr int LDS_STRIDE = HD + 8; // bf16 elements per staged row (pad against conflicts)
@@ -68,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void kv_write_kernel(KvWriteArgs a) {
     } else {
       for (int i = 0; i < 8; ++i) { kv[i] = (__bf16)0.0f; vv[i] = (__bf16)0.0f; }
     }
-    *reinterpret_cast<bf16x8*>(kc + kbase + (int64_t)tok * HD + ch * 8) = kv;
+    store16<NT>(kc + kbase + (int64_t)tok * HD + ch * 8, kv);
     *reinterpret_cast<bf16x8*>(&vtile[row * LDS_STRIDE + ch * 8]) = vv;
   }
   __syncthreads();
@@ -77,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void kv_write_kernel(KvWriteArgs a) {
     const int d = c / (kTok / 8), tc = c % (kTok / 8);
     bf16x8 out;
     for (int i = 0; i < 8; ++i) out[i] = vtile[(tc * 8 + i) * LDS_STRIDE + d];
-    *reinterpret_cast<bf16x8*>(vt + vbase + (int64_t)d * a.lpad + tok0 + tc * 8) = out;
+    store16<NT>(vt + vbase + (int64_t)d * a.lpad + tok0 + tc * 8, out);
   }
 }
 
@@ -87,12 +96,20 @@ hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream) {
   if (a.num_writes == 0) return hipSuccess;
   dim3 grid(a.lpad / kTok, a.num_writes, a.heads);
   dim3 block(kThreads);
+  auto go = [&](auto hd, auto fp32) {
+    constexpr int H = decltype(hd)::value;
+    constexpr bool F = decltype(fp32)::value;
+    if (a.stream_out) hipLaunchKernelGGL((kv_write_kernel<H, F, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((kv_write_kernel<H, F, false>), grid, block, 0, stream, a);
+  };
+  using I128 = std::integral_constant<int, 128>;
+  using I64 = std::integral_constant<int, 64>;
   if (a.head_dim == 128) {
-    if (a.src_fp32) hipLaunchKernelGGL((kv_write_kernel<128, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((kv_write_kernel<128, false>), grid, block, 0, stream, a);
+    if (a.src_fp32) go(I128{}, std::true_type{});
+    else go(I128{}, std::false_type{});
   } else {
-    if (a.src_fp32) hipLaunchKernelGGL((kv_write_kernel<64, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((kv_write_kernel<64, false>), grid, block, 0, stream, a);
+    if (a.src_fp32) go(I64{}, std::true_type{});
+    else go(I64{}, std::false_type{});
   }
   return hipGetLastError();
 }

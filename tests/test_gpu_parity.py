@@ -19,11 +19,13 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("hd", [64, 128])
 @pytest.mark.parametrize("src", ["fp32", "bf16"])
-def test_kv_write_layout(gpu_device, hd, src):
+@pytest.mark.parametrize("query_len", [0, 16])  # 16: decode-shaped plan, non-temporal cache stores
+def test_kv_write_layout(gpu_device, hd, src, query_len):
     import torch
-    log(f"kv_write layout hd={hd} src={src}")
+    log(f"kv_write layout hd={hd} src={src} query_len={query_len}")
     B, K, L, Cn, heads = 3, 2, 100, 37, 3
-    plan = wv.wave_plan(B=B, K=K, policy=wv.PROGRESSIVE, sched=wv.WAVE, chunk_len=L, cond_len=Cn)
+    plan = wv.wave_plan(B=B, K=K, policy=wv.PROGRESSIVE, sched=wv.WAVE, chunk_len=L, cond_len=Cn,
+                        query_len=query_len)
     inp = HostInputs(11, heads, hd, L, Cn)
     desc = plan.upload(gpu_device)
     cache = wv.KVCache(plan.num_phys_slots, heads, hd, plan.lpad(), gpu_device, fill=float("nan"))
