@@ -60,8 +60,12 @@ def gpu_chain(plan, B, L, heads, hd, noise, weights, scale, device, balance=Fals
 
 @pytest.mark.parametrize("heads,hd,L,layout", [(2, 64, 300, wv.X_CHUNK), (1, 128, 129, wv.X_ROUND),
                                                (3, 128, 200, wv.X_CHUNK), (4, 64, 64, wv.X_ROUND),
-                                               (2, 128, 300, wv.X_CHUNK), (4, 128, 520, wv.X_ROUND)])
+                                               (2, 128, 300, wv.X_CHUNK), (4, 128, 520, wv.X_ROUND),
+                                               (2, 128, 400, wv.X_ROUND)])
 def test_qkv_project_parity(gpu_device, heads, hd, L, layout):
+    # D = heads * hd: 128 and 384 take the 128-column kernel, 256 and 512 the
+    # 256-column one; L = 300 and 520 give a last row tile of at most 128 slot
+    # rows (dispatched last, half its waves idle), L = 400 one of 192 rows.
     """Q, K and V^T of one round against oracle.chain.project on the same bf16
     inputs, slot tails exactly zero, slots of other rounds untouched.  Bound
     per element: one bf16 rounding step (2^-7 relative) on top of the fp32
