@@ -471,6 +471,52 @@ def test_splitkv_grid_parity(gpu_device, policy, H, cond, L, qlen, heads, hd, sp
         compare(got[key][0], got[key][1], ref[key][0], ref[key][1], f"node {key}")
 
 
+def test_splitkv_workspace_reuse_and_garbage(gpu_device):
+    """The split-KV workspace needs no initialisation: calls on one workspace,
+    starting from random bytes, from all-ones bytes and from what earlier
+    calls left, give bitwise equal results that match the oracle (explicit
+    and automatic split counts; the automatic one leaves some splits with
+    empty key ranges at this size)."""
+    import torch
+    B, K, L, cond, qlen, heads, hd = 5, 3, 300, 70, 64, 2, 128
+    log(f"splitkv workspace reuse B={B} K={K} L={L} cond={cond} qlen={qlen}")
+    plan = wv.wave_plan(B=B, K=K, policy=wi.SAME_LEVEL, sched=wv.WAVE, chunk_len=L, cond_len=cond,
+                        query_len=qlen)
+    inp = HostInputs(777, heads, hd, L, cond, bf16=True, query_len=qlen)
+    scale = 1.0 / np.sqrt(hd)
+    desc = plan.upload(gpu_device)
+    cache = wv.KVCache(plan.num_phys_slots, heads, hd, plan.lpad(), gpu_device, fill=float("nan"))
+    target = max(range(plan.num_rounds), key=lambda t: len(plan.round_nodes(t)))
+    for t in range(target + 1):
+        ks, vs = zip(*[inp.kv(c, lv) for (c, lv, _p, _n) in plan.round_writes(t).tolist()])
+        wv.kv_write(plan, desc, t, cache, torch.from_numpy(np.concatenate(ks)).to(gpu_device, torch.bfloat16),
+                    torch.from_numpy(np.concatenate(vs)).to(gpu_device, torch.bfloat16))
+    nodes = plan.round_nodes(target).tolist()
+    q = torch.from_numpy(np.concatenate([inp.q(n[0], n[1]) for n in nodes])).to(gpu_device, torch.bfloat16)
+    results = {}
+    for splits in (3, 0):
+        nbytes, used = wv.splitkv_workspace_bytes(plan, target, heads, hd, splits)
+        assert used > 1
+        g = torch.Generator().manual_seed(splits)
+        ws = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g).to(gpu_device)
+        outs = []
+        for call in range(4):
+            if call == 2:
+                ws.fill_(255)
+            o, lse = wv.wave_attn_splitkv(plan, desc, target, cache, q, scale, num_splits=splits, workspace=ws)
+            torch.cuda.synchronize()
+            outs.append((o.float().cpu().numpy(), lse.cpu().numpy()))
+        for o, lse in outs[1:]:
+            assert np.array_equal(o, outs[0][0]) and np.array_equal(lse, outs[0][1])
+        results[used] = outs[0]
+    ref = oracle_rollout(B, K, wi.SAME_LEVEL, -1, L, cond, inp, scale, query_len=qlen,
+                         want={(n[0], n[1]) for n in nodes})
+    for used, (o, lse) in results.items():
+        for n in nodes:
+            a, b = n[4], n[4] + n[5]
+            compare(o[a:b], lse[:, a:b], ref[(n[0], n[1])][0], ref[(n[0], n[1])][1], f"splits {used} node {n[:2]}")
+
+
 def test_streamer_audio_decode_splitkv(gpu_device):
     """Decode-shaped Wan-Streamer round: the 64 audio rows of each chunk in round 7
     (U(6,1) over 23,352 keys, U(7,2) over 26,688 keys) with split-KV, all 40
