@@ -130,6 +130,9 @@ def main():
                     help="qkv_project against the plain bf16 product (torch.matmul) of the same shape, "
                          "one round per node count of the Wan2.1-1.3B pipelined plan")
     ap.add_argument("--layers", type=int, default=0, help="rollout layers (0 = the workload's)")
+    ap.add_argument("--no-fused-rms", action="store_true",
+                    help="with --chain, take each layer's input RMS from a pass over its rows instead of "
+                         "from the per-head sums of squares the previous attention wrote")
     ap.add_argument("--no-extra", action="store_true",
                     help="with workload 2, skip the Wan-Streamer round and audio decode timed after it")
     args = ap.parse_args()
@@ -384,6 +387,9 @@ def chain_bench(args, device):
         q = torch.empty((max_rows, w.heads, w.head_dim), dtype=torch.bfloat16, device=device)
         o = [torch.empty((max_rows, w.heads, w.head_dim), dtype=torch.bfloat16, device=device) for _ in range(2)]
         proj_ws = torch.empty(max_rows * 4 + 256, dtype=torch.uint8, device=device)
+        # per-head sums of squares of each layer's O: the next layer's RMS
+        sq = [torch.empty((max_rows, w.heads), dtype=torch.float32, device=device) for _ in range(2)]
+        fused = not args.no_fused_rms
         attn_bytes = max(wv.attn_workspace(plan, t, w.heads, w.head_dim)[0] for t in range(plan.num_rounds))
         attn_ws = torch.empty(max(attn_bytes, 1), dtype=torch.uint8, device=device)
         proj_ms = attn_ms = store_ms = 0.0
@@ -395,22 +401,23 @@ def chain_bench(args, device):
                 rows = int(plan.round_q_rows[t])
                 attn_flops += algorithmic_flops(plan, t, w.heads, w.head_dim) * layers
                 proj_flops += 2.0 * rows * D * 3 * D * layers
-                x, layout = state, wv.X_CHUNK
+                x, layout, x_sq = state, wv.X_CHUNK, None
                 for layer in range(layers):
                     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
                     ev[0].record(stream)
                     wv.qkv_project(plan, desc, t, caches[layer], x, weights[layer], q=q[:rows], x_layout=layout,
-                                   workspace=proj_ws, stream=stream)
+                                   workspace=proj_ws, stream=stream, row_sq=x_sq)
                     ev[1].record(stream)
                     ob = o[layer & 1][:rows]
+                    o_sq = sq[layer & 1] if fused else None
                     wv.wave_attn(plan, desc, t, caches[layer], q[:rows], w.scale, o=ob, want_lse=False,
-                                 stream=stream, workspace=attn_ws)
+                                 stream=stream, workspace=attn_ws, row_sq=o_sq)
                     ev[2].record(stream)
                     ev[2].synchronize()
                     proj_ms += ev[0].elapsed_time(ev[1])
                     attn_ms += ev[1].elapsed_time(ev[2])
                     round_ms[t] += ev[0].elapsed_time(ev[2])
-                    x, layout = ob.view(rows, D), wv.X_ROUND
+                    x, layout, x_sq = ob.view(rows, D), wv.X_ROUND, o_sq
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
                 wv.chain_store(plan, desc, t, o[(layers - 1) & 1][:rows], state, stream=stream)
@@ -425,6 +432,7 @@ def chain_bench(args, device):
         calls = plan.num_rounds * layers
         res = {
             "policy": wi.POLICY_NAMES[policy], "layers": layers, "rounds": plan.num_rounds,
+            "rms_from_attention": fused,
             "total_ms": round(total, 3), "ms_per_round": round(total / plan.num_rounds, 3),
             "ms_per_chunk": round(total / w.B, 3),
             "attention_tflops": round(attn_flops / (attn_ms * 1e-3) / 1e12, 1),

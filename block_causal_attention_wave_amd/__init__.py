@@ -197,14 +197,18 @@ def attn_workspace(plan: Plan, round: int, heads: int, head_dim: int, compute_un
 
 
 def wave_attn(plan: Plan, d_desc, round: int, cache: KVCache, q, scale: float, o=None, lse=None,
-              want_lse=True, stream=None, balance=True, workspace=None):
+              want_lse=True, stream=None, balance=True, workspace=None, row_sq=None):
     """Attention of round `round`: q [rows, heads, d] (bf16 or fp32) -> (o bf16, lse fp32 [heads, rows]).
 
     balance: cut the round's trailing work items into key ranges when that
     shortens it (results then equal the unbalanced ones up to rounding); the
     workspace (uint8 tensor of attn_workspace() bytes) is allocated here when
     not given.  balance=False keeps each node's result bitwise independent of
-    the schedule."""
+    the schedule.
+
+    row_sq: None, or an fp32 tensor [rows, heads] that receives each output
+    row's per-head sum of squares of the bf16 O (wave_attn_chain), for the
+    next layer's qkv_project(row_sq=...)."""
     import torch
     o, lse = _attn_outputs(plan, round, cache, q, o, lse, want_lse)
     ws_ptr, ws_bytes = 0, 0
@@ -214,11 +218,21 @@ def wave_attn(plan: Plan, d_desc, round: int, cache: KVCache, q, scale: float, o
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
         if workspace is not None:
             ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    _lib.check(_lib.load().wave_attn(plan.handle, C.c_void_p(d_desc.data_ptr()), round, C.byref(cache.c),
-                                     C.c_void_p(q.data_ptr()), _dtype_code(q), q.stride(0),
-                                     C.c_void_p(o.data_ptr()),
-                                     C.c_void_p(lse.data_ptr() if lse is not None else 0),
-                                     float(scale), C.c_void_p(ws_ptr), ws_bytes, _stream_ptr(stream)))
+    lse_ptr = C.c_void_p(lse.data_ptr() if lse is not None else 0)
+    if row_sq is None:
+        _lib.check(_lib.load().wave_attn(plan.handle, C.c_void_p(d_desc.data_ptr()), round, C.byref(cache.c),
+                                         C.c_void_p(q.data_ptr()), _dtype_code(q), q.stride(0),
+                                         C.c_void_p(o.data_ptr()), lse_ptr, float(scale), C.c_void_p(ws_ptr),
+                                         ws_bytes, _stream_ptr(stream)))
+    else:
+        if (row_sq.dtype != torch.float32 or not row_sq.is_contiguous()
+                or row_sq.numel() < int(plan.round_q_rows[round]) * cache.heads):
+            raise ValueError("row_sq must be a contiguous float32 tensor of at least rows * heads elements")
+        _lib.check(_lib.load().wave_attn_chain(plan.handle, C.c_void_p(d_desc.data_ptr()), round,
+                                               C.byref(cache.c), C.c_void_p(q.data_ptr()), _dtype_code(q),
+                                               q.stride(0), C.c_void_p(o.data_ptr()), lse_ptr, float(scale),
+                                               C.c_void_p(row_sq.data_ptr()), C.c_void_p(ws_ptr), ws_bytes,
+                                               _stream_ptr(stream)))
     return o, lse
 
 
@@ -323,12 +337,13 @@ def qkv_project_workspace_bytes(plan: Plan, round: int) -> int:
 
 
 def qkv_project(plan: Plan, d_desc, round: int, cache: KVCache, x, w, q=None, x_layout=X_ROUND,
-                workspace=None, stream=None):
+                workspace=None, stream=None, row_sq=None):
     """QKV projection of every node of round `round` at one layer: K/V into the
     nodes' own slots of `cache`, Q returned ([rows, heads, head_dim] bf16).
 
     x: bf16 input rows, [round rows, D] (X_ROUND) or per-chunk state
-    [B, chunk_len, D] (X_CHUNK); w: bf16 [3D, D]."""
+    [B, chunk_len, D] (X_CHUNK); w: bf16 [3D, D].  row_sq: None, or the
+    row_sq that wave_attn(row_sq=...) wrote with x as its o (X_ROUND only)."""
     import torch
     rows = int(plan.round_q_rows[round])
     if q is None:
@@ -337,7 +352,9 @@ def qkv_project(plan: Plan, d_desc, round: int, cache: KVCache, x, w, q=None, x_
     if workspace is None:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=x.device)
     _lib.check(_lib.load().qkv_project(plan.handle, C.c_void_p(d_desc.data_ptr()), round, C.byref(cache.c),
-                                       C.c_void_p(x.data_ptr()), int(x_layout), C.c_void_p(w.data_ptr()),
+                                       C.c_void_p(x.data_ptr()), int(x_layout),
+                                       C.c_void_p(row_sq.data_ptr() if row_sq is not None else 0),
+                                       C.c_void_p(w.data_ptr()),
                                        C.c_void_p(q.data_ptr()), C.c_void_p(workspace.data_ptr()),
                                        workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
     return q

@@ -25,8 +25,8 @@ WAVE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 EXPORTS = ("wave_plan", "wave_plan_view_get", "wave_plan_desc_size", "wave_plan_desc_pack",
            "wave_plan_destroy", "kv_write", "wave_attn_workspace", "wave_attn", "wave_attn_splitkv_workspace",
-           "wave_round", "wave_attn_splitkv", "wave_attn_splitkv_noalloc", "qkv_project_workspace",
-           "qkv_project", "chain_store", "wave_last_error")
+           "wave_round", "wave_attn_splitkv", "wave_attn_splitkv_noalloc", "wave_attn_chain",
+           "qkv_project_workspace", "qkv_project", "chain_store", "wave_last_error")
 
 
 class PlanParams(C.Structure):
@@ -121,8 +121,12 @@ def load() -> C.CDLL:
     lib.wave_attn_splitkv_noalloc.restype = C.c_int32
     lib.qkv_project_workspace.argtypes = [C.c_void_p, C.c_int32, C.POINTER(C.c_size_t)]
     lib.qkv_project_workspace.restype = C.c_int32
+    lib.wave_attn_chain.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.POINTER(KvCache),
+                                    C.c_void_p, C.c_int32, C.c_int64, C.c_void_p, C.c_void_p,
+                                    C.c_float, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+    lib.wave_attn_chain.restype = C.c_int32
     lib.qkv_project.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.POINTER(KvCache), C.c_void_p, C.c_int32,
-                                C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+                                C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
     lib.qkv_project.restype = C.c_int32
     lib.chain_store.argtypes = [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]
     lib.chain_store.restype = C.c_int32

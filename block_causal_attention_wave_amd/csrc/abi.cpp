@@ -348,6 +348,21 @@ int32_t wave_attn(const wave_plan_t* plan, const void* d_desc, int32_t round, co
   return ok();
 }
 
+int32_t wave_attn_chain(const wave_plan_t* plan, const void* d_desc, int32_t round, const wave_kv_cache* cache,
+                        const void* q, int32_t q_dtype, int64_t q_row_stride, void* o, float* lse, float scale,
+                        float* row_sq, void* workspace, size_t workspace_bytes, void* stream) {
+  wave::AttnArgs a;
+  const int32_t rc = attn_prepare(plan, d_desc, round, cache, q, q_dtype, q_row_stride, o, lse, scale, workspace,
+                                  workspace_bytes, "wave_attn_chain", a);
+  if (rc != WAVE_OK) return rc;
+  if (row_sq && (reinterpret_cast<uintptr_t>(row_sq) & 3u) != 0)
+    return set_error(WAVE_ERR_UNSUPPORTED, "wave_attn_chain: row_sq must be 4-byte aligned");
+  a.row_sq = row_sq;
+  const hipError_t e = wave::launch_wave_attn(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return set_error(WAVE_ERR_HIP, std::string("wave_attn_chain: ") + hipGetErrorString(e));
+  return ok();
+}
+
 int32_t wave_round(const wave_plan_t* plan, const void* d_desc, int32_t round, int32_t num_layers,
                    const wave_kv_cache* caches, const void* const* k_src, const void* const* v_src, int32_t src_dtype,
                    int64_t src_row_stride, const void* const* q, int32_t q_dtype, int64_t q_row_stride,
@@ -500,7 +515,7 @@ int32_t qkv_project_workspace(const wave_plan_t* plan, int32_t round, size_t* by
 }
 
 int32_t qkv_project(const wave_plan_t* plan, const void* d_desc, int32_t round, const wave_kv_cache* cache,
-                    const void* x, int32_t x_layout, const void* w, void* q, void* workspace,
+                    const void* x, int32_t x_layout, const float* row_sq, const void* w, void* q, void* workspace,
                     size_t workspace_bytes, void* stream) {
   const std::string f("qkv_project");
   int32_t rc = check_common(plan, d_desc, round, cache, "qkv_project");
@@ -513,6 +528,10 @@ int32_t qkv_project(const wave_plan_t* plan, const void* d_desc, int32_t round, 
     return set_error(WAVE_ERR_INVALID_ARG, f + ": x_layout must be WAVE_X_ROUND or WAVE_X_CHUNK");
   if (!aligned16(x) || !aligned16(w) || !aligned16(q))
     return set_error(WAVE_ERR_UNSUPPORTED, f + ": x, w and q must be 16-byte aligned");
+  if (row_sq && x_layout != WAVE_X_ROUND)
+    return set_error(WAVE_ERR_INVALID_ARG, f + ": row_sq goes with x_layout WAVE_X_ROUND (x = wave_attn_chain's o)");
+  if (row_sq && (reinterpret_cast<uintptr_t>(row_sq) & 3u) != 0)
+    return set_error(WAVE_ERR_UNSUPPORTED, f + ": row_sq must be 4-byte aligned");
   const int64_t D = static_cast<int64_t>(cache->heads) * cache->head_dim;
   if (D % 128 != 0) return set_error(WAVE_ERR_UNSUPPORTED, f + ": heads * head_dim must be a multiple of 128");
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
@@ -547,6 +566,7 @@ int32_t qkv_project(const wave_plan_t* plan, const void* d_desc, int32_t round, 
   a.vt = cache->vt;
   a.q = q;
   a.row_scale = static_cast<float*>(workspace);
+  a.row_sq = row_sq;
   const hipError_t e = wave::launch_qkv_project(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return set_error(WAVE_ERR_HIP, f + ": " + hipGetErrorString(e));
   return ok();

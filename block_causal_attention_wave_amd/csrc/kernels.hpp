@@ -58,6 +58,10 @@ struct AttnArgs {
   int32_t part_rows;
   float* part_o;
   float* part_lse;
+  // Optional (nullptr: none): fp32 [rows][heads], per output row and head
+  // the sum of squares of the row's bf16 O values over head_dim (the next
+  // layer's RMS statistics in the toy chain).
+  float* row_sq;
 };
 
 // Output tile of one qkv_project workgroup: tokens x projection columns.
@@ -80,6 +84,10 @@ struct ProjArgs {
   void* vt;
   void* q;
   float* row_scale;
+  // Optional (nullptr: 1/rms computed from x into row_scale first): fp32
+  // [round rows][heads] sums of squares of x's rows per head, as wave_attn
+  // writes them for its O; x must then be the round-packed O.
+  const float* row_sq;
 };
 
 // Copy of each node's output rows o[q_offset ..] to its chunk's state rows.

@@ -12,7 +12,9 @@
 // K/V copy pass is needed; Q goes to the round's packed query rows.
 //
 // Kernels:
-//   row_scale_kernel  1 / rms of every input row (one wave per row).
+//   row_scale_kernel  1 / rms of every input row (one wave per row); or
+//   row_scale_from_sq_kernel  the same from per-head sums of squares of the
+//                     rows that the attention wrote with its O (wave_attn_chain).
 //   qkv_gemm_kernel   one workgroup per (node, 256-token tile, 128-column
 //                     tile), 8 waves of 64x64: bf16 MFMA 32x32x16, fp32
 //                     accumulation, a three-stage LDS ring of 256x64 A and
@@ -77,6 +79,30 @@ __global__ __launch_bounds__(256) void row_scale_kernel(ProjArgs a) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
   if (lane == 0) a.row_scale[q_offset + r] = 1.0f / __builtin_sqrtf(ss / (float)a.model_dim + 1e-6f);
+}
+
+// The same 1 / rms from per-head sums of squares of the rows (as
+// wave_attn_chain writes them for its O, which is then x): one thread per
+// row, grid (row blocks, nodes).
+__global__ __launch_bounds__(256) void row_scale_from_sq_kernel(ProjArgs a) {
+  const int node = a.node_begin + blockIdx.y;
+  const int32_t* nd = a.nodes + kDescNodeWords * node;
+  const int q_offset = nd[0], L = nd[1];
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= L) return;
+  const float* sq = a.row_sq + (int64_t)(q_offset + r) * a.heads;
+  // four independent chains, so that the loads of a group issue together
+  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+  int h = 0;
+  for (; h + 4 <= a.heads; h += 4) {
+    s0 += sq[h];
+    s1 += sq[h + 1];
+    s2 += sq[h + 2];
+    s3 += sq[h + 3];
+  }
+  for (; h < a.heads; ++h) s0 += sq[h];
+  const float ss = (s0 + s1) + (s2 + s3);
+  a.row_scale[q_offset + r] = 1.0f / __builtin_sqrtf(ss / (float)a.model_dim + 1e-6f);
 }
 
 template <int HD>
@@ -406,12 +432,35 @@ __global__ __launch_bounds__(THREADS, 1) void qkv_gemm_wide_kernel(ProjArgs a) {
   const int part = c0 / D;  // 0: Q, 1: K, 2: V (D is a multiple of TN)
   // 1/rms of token (lane & 31) of each of the wave's 32-token blocks (0 past
   // the chunk's tokens), fetched now so that the epilogue does not wait.
-  float rsc[4];
+  // With per-head sums of squares (x = the attention's O that wrote them),
+  // the tile's 256 scales are formed here instead, after the first tile's
+  // loads are issued, and kept in LDS: two threads per row, one of every
+  // other head each.
+  __shared__ float rs_lds[TM];
+  const bool from_sq = a.row_sq != nullptr;
+  float rsc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (!from_sq) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = r0 + wr * 128 + i * 32 + (lane & 31);
-    rsc[i] = r < L ? a.row_scale[q_offset + r] : 0.0f;
+    for (int i = 0; i < 4; ++i) {
+      const int r = r0 + wr * 128 + i * 32 + (lane & 31);
+      rsc[i] = r < L ? a.row_scale[q_offset + r] : 0.0f;
+    }
   }
+  auto scales_from_sq = [&]() __attribute__((always_inline)) {
+    const int row = tid >> 1, hp = tid & 1;
+    const int r = r0 + row;
+    const float* sq = a.row_sq + (int64_t)(q_offset + min(r, L - 1)) * a.heads;
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int h = hp + 2 * k;
+      v[k] = h < a.heads ? sq[h] : 0.0f;
+    }
+    float ss = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+    for (int h = hp + 16; h < a.heads; h += 2) ss += sq[h];
+    ss += __shfl_xor(ss, 1, 64);
+    if (hp == 0) rs_lds[row] = r < L ? 1.0f / __builtin_sqrtf(ss / (float)a.model_dim + 1e-6f) : 0.0f;
+  };
 
   // Two stages: after the barrier of k-step ks every wave is done with ks-1,
   // whose stage receives ks+1 while ks is multiplied.
@@ -419,6 +468,7 @@ __global__ __launch_bounds__(THREADS, 1) void qkv_gemm_wide_kernel(ProjArgs a) {
   auto kloop = [&](auto tr_tag) __attribute__((always_inline)) {
   constexpr bool TR = decltype(tr_tag)::value;
   issue(0, 0);
+  if (from_sq) scales_from_sq();  // its loads' latency overlaps the first tile's; the k-loop's barriers publish it
   int stage = 0;
   for (int ks = 0; ks < nk; ++ks) {
     __builtin_amdgcn_s_waitcnt(kWaitExp);  // this thread's loads of k-step ks have landed
@@ -466,6 +516,10 @@ __global__ __launch_bounds__(THREADS, 1) void qkv_gemm_wide_kernel(ProjArgs a) {
   if (part == 2) kloop(std::false_type{});
   else kloop(std::true_type{});
   barrier();  // the epilogue reuses the stages
+  if (from_sq) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rsc[i] = rs_lds[wr * 128 + i * 32 + (lane & 31)];
+  }
 
   // Epilogue: scale by 1/rms, round, stage in LDS (column-major for V), then
   // 16-byte stores to Q, K or V^T.  Q/K lanes hold token (lane & 31) of each
@@ -565,11 +619,17 @@ __global__ __launch_bounds__(256) void chain_store_kernel(StoreArgs a) {
 
 hipError_t launch_qkv_project(const ProjArgs& a, hipStream_t stream) {
   if (a.num_nodes == 0) return hipSuccess;
-  dim3 sgrid((unsigned)((a.max_rows + 3) / 4), (unsigned)a.num_nodes);
-  hipLaunchKernelGGL(row_scale_kernel, sgrid, dim3(256), 0, stream, a);
+  const bool wide_tiles = a.model_dim % wide::TN == 0;
+  if (a.row_sq == nullptr) {
+    dim3 sgrid((unsigned)((a.max_rows + 3) / 4), (unsigned)a.num_nodes);
+    hipLaunchKernelGGL(row_scale_kernel, sgrid, dim3(256), 0, stream, a);
+  } else if (!wide_tiles) {  // the wide kernel forms the scales from row_sq itself
+    dim3 sgrid((unsigned)((a.max_rows + 255) / 256), (unsigned)a.num_nodes);
+    hipLaunchKernelGGL(row_scale_from_sq_kernel, sgrid, dim3(256), 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.model_dim % wide::TN == 0) {
+  if (wide_tiles) {
     // 256-wide column tiles: a tile never straddles the Q / K / V parts
     ProjArgs w = a;
     w.col_tiles = 3 * a.model_dim / wide::TN;

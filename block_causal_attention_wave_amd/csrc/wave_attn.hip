@@ -658,16 +658,26 @@ void wave_attn_kernel(AttnArgs a) {
           if (lane < 32) a.part_lse[((int64_t)split * a.heads + h) * a.part_rows + prow] = lse;
         } else {
           __bf16* orow = static_cast<__bf16*>(a.o) + grow * orow_stride + (int64_t)h * HD;
+          float sq = 0.0f;  // sum of squares of the row's bf16 outputs (this lane's half)
   #pragma unroll
           for (int db = 0; db < C::ND; ++db)
   #pragma unroll
             for (int g = 0; g < 4; ++g) {
               bf16x4 v;
   #pragma unroll
-              for (int i = 0; i < 4; ++i) v[i] = (__bf16)(o[db][qb][4 * g + i] * inv);
+              for (int i = 0; i < 4; ++i) {
+                v[i] = (__bf16)(o[db][qb][4 * g + i] * inv);
+                sq = __builtin_fmaf((float)v[i], (float)v[i], sq);
+              }
               *reinterpret_cast<bf16x4*>(orow + db * 32 + g * 8 + (lane >> 5) * 4) = v;
             }
           if (a.lse != nullptr && lane < 32) a.lse[(int64_t)h * a.lse_stride + grow] = lse;
+          if (a.row_sq != nullptr) {
+            // lanes l and l^32 hold the two halves of the row's dims (and
+            // share r, so both take this branch)
+            sq = halfwave_sum(sq);
+            if (lane < 32) a.row_sq[grow * a.heads + h] = sq;
+          }
         }
       }
     }
@@ -720,9 +730,19 @@ __global__ __launch_bounds__(256) void wave_attn_combine_kernel(AttnArgs a) {
   }
   const float inv = 1.0f / wsum;
   bf16x8 out;
-  for (int i = 0; i < 8; ++i) out[i] = (__bf16)(acc[i] * inv);
+  float sq = 0.0f;
+  for (int i = 0; i < 8; ++i) {
+    out[i] = (__bf16)(acc[i] * inv);
+    sq = __builtin_fmaf((float)out[i], (float)out[i], sq);
+  }
   *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(a.o) + (row * a.heads + h) * HD + ch * 8) = out;
   if (ch == 0 && a.lse != nullptr) a.lse[(int64_t)h * rows + row] = smax + __logf(wsum);
+  if (a.row_sq != nullptr) {
+    // The `chunks` threads of one (row, head) are consecutive and aligned in
+    // the wave, and return early (above) all together or not at all.
+    for (int m = chunks / 2; m >= 1; m >>= 1) sq += __shfl_xor(sq, m, chunks);
+    if (ch == 0) a.row_sq[row * a.heads + h] = sq;
+  }
 }
 
 template <bool TAIL>

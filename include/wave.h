@@ -296,6 +296,18 @@ int32_t wave_attn_splitkv_noalloc(const wave_plan_t* plan, const void* d_desc, i
 #define WAVE_X_ROUND 0 /* x is [round_q_rows][D], packed like the round's Q (e.g. the previous layer's O) */
 #define WAVE_X_CHUNK 1 /* x is per-chunk state [B][chunk_len][D] (chain_store's layout) */
 
+/* wave_attn that also hands the next layer its RMS statistics: row_sq
+ * (device fp32 [round_q_rows][heads], 4-byte aligned, or NULL for none)
+ * receives, for every output row and head, the sum over head_dim of the
+ * squares of the bf16 O values written.  The next layer's qkv_project takes
+ * it with x = this o, instead of a pass over x's rows (the per-token
+ * normalisation of the toy chain; fused here into the kernel that produces
+ * the rows).  Other arguments, results and behaviour as for wave_attn. */
+int32_t wave_attn_chain(const wave_plan_t* plan, const void* d_desc, int32_t round,
+                        const wave_kv_cache* cache, const void* q, int32_t q_dtype,
+                        int64_t q_row_stride, void* o, float* lse, float scale, float* row_sq,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace of qkv_project for round `round`: one fp32 per query row. */
 int32_t qkv_project_workspace(const wave_plan_t* plan, int32_t round, size_t* bytes);
 
@@ -304,6 +316,9 @@ int32_t qkv_project_workspace(const wave_plan_t* plan, int32_t round, size_t* by
  *          last entry of its gather list), tokens [chunk_len, lpad) zeroed.
  *          Replaces kv_write for chain rounds.
  *   x    : device bf16 input rows, layout x_layout.
+ *   row_sq: NULL, or wave_attn_chain's row_sq of the call whose o is x
+ *          (x_layout must then be WAVE_X_ROUND): rms(row) is taken as
+ *          sqrt(sum_h row_sq[row][h] / D + 1e-6) instead of from x's rows.
  *   w    : device bf16 [3D][D]; row o holds output column o's weights
  *          (o < D: Q, then K, then V; column = head * head_dim + dim).
  *   q    : device bf16 [round_q_rows][heads][head_dim] (wave_attn's q).
@@ -311,8 +326,8 @@ int32_t qkv_project_workspace(const wave_plan_t* plan, int32_t round, size_t* by
  * D must be a multiple of 128.  Asynchronous on `stream`. */
 int32_t qkv_project(const wave_plan_t* plan, const void* d_desc, int32_t round,
                     const wave_kv_cache* cache, const void* x, int32_t x_layout,
-                    const void* w, void* q, void* workspace, size_t workspace_bytes,
-                    void* stream);
+                    const float* row_sq, const void* w, void* q, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 /* state[chunk(n)] = o[rows of n] for every node n of round `round`:
  *   o    : device bf16 [round_q_rows][model_dim] (wave_attn's o of the last layer).

@@ -77,8 +77,12 @@ static long exercise(const wave_plan_params& prm) {
       wave_kv_cache c2{fake(0x100000), fake(0x200000), v.num_phys_slots, 2, 64, lpad};
       size_t pw = 0;
       CHECK(qkv_project_workspace(plan, t, &pw) == WAVE_OK);
-      CHECK(qkv_project(plan, d, t, &c2, fake(0xa00000), WAVE_X_ROUND, fake(0xb00000), fake(0x600000),
+      CHECK(qkv_project(plan, d, t, &c2, fake(0xa00000), WAVE_X_ROUND, nullptr, fake(0xb00000), fake(0x600000),
                         fake(0xc00000), pw, st) == WAVE_OK);
+      CHECK(wave_attn_chain(plan, d, t, &c2, fake(0x600000), WAVE_DTYPE_BF16, 128, fake(0x700000), nullptr, 0.1f,
+                            static_cast<float*>(fake(0xe00000)), nullptr, 0, st) == WAVE_OK);
+      CHECK(qkv_project(plan, d, t, &c2, fake(0x700000), WAVE_X_ROUND, static_cast<const float*>(fake(0xe00000)),
+                        fake(0xb00000), fake(0x600000), fake(0xc00000), pw, st) == WAVE_OK);
       CHECK(chain_store(plan, d, t, 128, fake(0x700000), fake(0xd00000), st) == WAVE_OK);
     }
     // invalid arguments are refused on the host

@@ -64,6 +64,7 @@ hipError_t launch_wave_attn(const AttnArgs& a, hipStream_t) {
 
 hipError_t launch_qkv_project(const ProjArgs& a, hipStream_t) {
   STUB_CHECK(a.num_nodes >= 0 && a.model_dim % 128 == 0 && a.row_scale && a.x && a.w && a.q);
+  if (a.row_sq) STUB_CHECK(a.x_chunk == 0);
   ++stub::launches;
   return hipSuccess;
 }

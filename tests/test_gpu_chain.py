@@ -30,8 +30,12 @@ def _inputs(key, B, L, heads, hd, layers):
     return noise, weights
 
 
-def gpu_chain(plan, B, L, heads, hd, noise, weights, scale, device, balance=False):
-    """Run the chain over `plan` on the GPU; return {(chunk, level): [O per layer as [L, heads, hd] fp32]}."""
+def gpu_chain(plan, B, L, heads, hd, noise, weights, scale, device, balance=False, fused_rms=True):
+    """Run the chain over `plan` on the GPU; return {(chunk, level): [O per layer as [L, heads, hd] fp32]}.
+
+    fused_rms: a layer after the first takes its input rows' RMS from the
+    per-head sums of squares that the previous layer's attention wrote with
+    its O (wave_attn row_sq), instead of a pass over the rows."""
     import torch
     D = heads * hd
     layers = len(weights)
@@ -40,16 +44,19 @@ def gpu_chain(plan, B, L, heads, hd, noise, weights, scale, device, balance=Fals
               for _ in range(layers)]
     w_dev = [torch.from_numpy(w).to(device=device, dtype=torch.bfloat16) for w in weights]
     state = torch.from_numpy(np.stack([noise[c] for c in range(B)])).to(device=device, dtype=torch.bfloat16)
+    max_rows = int(plan.round_q_rows.max())
+    sq = [torch.full((max_rows, heads), float("nan"), device=device) for _ in range(2)]
     outs = {}
     for t in range(plan.num_rounds):
         rows = int(plan.round_q_rows[t])
-        x, layout = state, wv.X_CHUNK
+        x, layout, x_sq = state, wv.X_CHUNK, None
         per_layer = []
         for layer in range(layers):
-            q = wv.qkv_project(plan, desc, t, caches[layer], x, w_dev[layer], x_layout=layout)
-            o, _ = wv.wave_attn(plan, desc, t, caches[layer], q, scale, balance=balance)
+            q = wv.qkv_project(plan, desc, t, caches[layer], x, w_dev[layer], x_layout=layout, row_sq=x_sq)
+            o_sq = sq[layer & 1] if fused_rms else None
+            o, _ = wv.wave_attn(plan, desc, t, caches[layer], q, scale, balance=balance, row_sq=o_sq)
             per_layer.append(o)
-            x, layout = o.view(rows, D), wv.X_ROUND
+            x, layout, x_sq = o.view(rows, D), wv.X_ROUND, o_sq
         wv.chain_store(plan, desc, t, per_layer[-1], state)
         torch.cuda.synchronize()
         for n in plan.round_nodes(t).tolist():
@@ -139,6 +146,65 @@ def test_chain_store_copies_node_rows(gpu_device):
             assert (state[c] == -1).all()
 
 
+@pytest.mark.parametrize("balance", [False, True])
+def test_attention_row_sq_feeds_projection(gpu_device, balance):
+    """wave_attn's row_sq (wave_attn_chain) against the host sum over head_dim
+    of the squares of the bf16 O it returned (fp32 sums of 64 or 128 exact
+    squares: relative error below 2^-17), with and without the tail-balancing
+    merge kernel writing part of the rows; then qkv_project of the next layer
+    taking the RMS from row_sq matches qkv_project taking it from the rows to
+    one bf16 step (the two 1/rms differ by a few fp32 roundings), and the
+    oracle's projection within its bound."""
+    import torch
+    heads, hd, L = 4, 128, 520
+    D = heads * hd
+    plan = wv.wave_plan(B=5, K=3, policy=wi.PROGRESSIVE, sched=wv.WAVE, chunk_len=L)
+    t = max(range(plan.num_rounds), key=lambda r: len(plan.round_nodes(r)))
+    rows = int(plan.round_q_rows[t])
+    nodes = plan.round_nodes(t).tolist()
+    log(f"row_sq balance={balance} round {t} rows {rows}")
+    rng = np.random.default_rng(5)
+    desc = plan.upload(gpu_device)
+    cache = wv.KVCache(plan.num_phys_slots, heads, hd, plan.lpad(), gpu_device, fill=0.0)
+    for r in range(t + 1):
+        n_new = sum(int(wr[3]) for wr in plan.round_writes(r).tolist())
+        k = torch.from_numpy(bf16(rng.standard_normal((n_new, heads, hd)))).to(gpu_device, torch.bfloat16)
+        v = torch.from_numpy(bf16(rng.standard_normal((n_new, heads, hd)))).to(gpu_device, torch.bfloat16)
+        wv.kv_write(plan, desc, r, cache, k, v)
+    q = torch.from_numpy(bf16(rng.standard_normal((rows, heads, hd)))).to(gpu_device, torch.bfloat16)
+    sq = torch.full((rows, heads), float("nan"), device=gpu_device)
+    o, _ = wv.wave_attn(plan, desc, t, cache, q, 1.0 / math.sqrt(hd), balance=balance, row_sq=sq)
+    torch.cuda.synchronize()
+    o64 = o.float().cpu().numpy().astype(np.float64)
+    want = (o64 * o64).sum(axis=2)
+    got = sq.cpu().numpy()
+    assert np.isfinite(got).all()
+    assert np.allclose(got, want, rtol=2.0 ** -17, atol=0.0), float(np.abs(got - want).max())
+    # the next layer's projection, RMS from row_sq against RMS from the rows
+    w = bf16(rng.standard_normal((3 * D, D)) / math.sqrt(D))
+    w_dev = torch.from_numpy(w).to(gpu_device, torch.bfloat16)
+    c1 = wv.KVCache(plan.num_phys_slots, heads, hd, plan.lpad(), gpu_device, fill=float("nan"))
+    c2 = wv.KVCache(plan.num_phys_slots, heads, hd, plan.lpad(), gpu_device, fill=float("nan"))
+    x = o.view(rows, D)
+    q1 = wv.qkv_project(plan, desc, t, c1, x, w_dev, x_layout=wv.X_ROUND, row_sq=sq)
+    q2 = wv.qkv_project(plan, desc, t, c2, x, w_dev, x_layout=wv.X_ROUND)
+    torch.cuda.synchronize()
+    for a, b in ((q1, q2), (c1.k, c2.k), (c1.vt, c2.vt)):
+        a, b = a.float().cpu().numpy(), b.float().cpu().numpy()
+        assert np.array_equal(np.isnan(a), np.isnan(b))
+        a, b = np.nan_to_num(a), np.nan_to_num(b)
+        assert (np.abs(a - b) <= 2.0 ** -7 * np.abs(b)).all()
+    q1 = q1.float().cpu().numpy()
+    for n in nodes:
+        a = o64[n[4]:n[4] + n[5]].reshape(n[5], D)
+        qo, _, _ = oc.project(a, w.astype(np.float64), heads, hd)
+        inv = 1.0 / np.sqrt(np.mean(a * a, axis=1) + 1e-6)
+        acc = ((D * 2.0 ** -24) * (np.abs(a) @ np.abs(w.astype(np.float64)).T) * inv[:, None])[:, :D]
+        acc = acc.reshape(n[5], heads, hd)
+        err = np.abs(q1[n[4]:n[4] + n[5]] - qo)
+        assert (err <= 2.0 ** -7 * (np.abs(qo) + acc) + acc).all(), (n[0], n[1])
+
+
 CHAIN_GRID = [
     # policy, B, K, L, heads, hd, layers
     (wi.PROGRESSIVE, 3, 2, 160, 2, 64, 2),
@@ -148,15 +214,17 @@ CHAIN_GRID = [
 ]
 
 
+@pytest.mark.parametrize("fused_rms", [True, False])
 @pytest.mark.parametrize("policy,B,K,L,heads,hd,layers", CHAIN_GRID)
-def test_chain_matches_oracle(gpu_device, policy, B, K, L, heads, hd, layers):
+def test_chain_matches_oracle(gpu_device, policy, B, K, L, heads, hd, layers, fused_rms):
     """Every node's per-layer attention output of a whole chain against the
-    independent fp64 chain oracle."""
+    independent fp64 chain oracle, with the RMS of a layer's input taken from
+    the previous attention's per-head sums of squares or from the rows."""
     noise, weights = _inputs(40 + L, B, L, heads, hd, layers)
     scale = 1.0 / math.sqrt(hd)
     plan = wv.wave_plan(B=B, K=K, policy=policy, sched=wv.WAVE, chunk_len=L)
-    log(f"chain policy={policy} B={B} K={K} L={L} heads={heads} hd={hd} layers={layers}")
-    got = gpu_chain(plan, B, L, heads, hd, noise, weights, scale, gpu_device)
+    log(f"chain policy={policy} B={B} K={K} L={L} heads={heads} hd={hd} layers={layers} fused_rms={fused_rms}")
+    got = gpu_chain(plan, B, L, heads, hd, noise, weights, scale, gpu_device, fused_rms=fused_rms)
     p = op.Params(B, K, policy, op.SERIAL, -1, L, 0, 0)
     ref = oc.chain_rollout(p, op.oracle_plan(p), layers, heads, hd, lambda c: noise[c].astype(np.float64),
                            lambda l: weights[l].astype(np.float64), scale)
@@ -274,14 +342,16 @@ def _device_chain(plan, w, layers, device, policy):
               for _ in range(layers)]
     weights = [wi.device_chain_weight(w.key, l, D, device) for l in range(layers)]
     state = torch.stack([wi.device_chain_noise(w.key, c, w.chunk_len, D, device) for c in range(w.B)])
+    sq = [torch.empty((int(plan.round_q_rows.max()), w.heads), device=device) for _ in range(2)]
     outs = {}
     for t in range(plan.num_rounds):
         rows = int(plan.round_q_rows[t])
-        x, layout = state, wv.X_CHUNK
+        x, layout, x_sq = state, wv.X_CHUNK, None
         for layer in range(layers):
-            q = wv.qkv_project(plan, desc, t, caches[layer], x, weights[layer], x_layout=layout)
-            o, _ = wv.wave_attn(plan, desc, t, caches[layer], q, w.scale, want_lse=False, balance=False)
-            x, layout = o.view(rows, D), wv.X_ROUND
+            q = wv.qkv_project(plan, desc, t, caches[layer], x, weights[layer], x_layout=layout, row_sq=x_sq)
+            o, _ = wv.wave_attn(plan, desc, t, caches[layer], q, w.scale, want_lse=False, balance=False,
+                                row_sq=sq[layer & 1])
+            x, layout, x_sq = o.view(rows, D), wv.X_ROUND, sq[layer & 1]
         wv.chain_store(plan, desc, t, o, state)
         for n in plan.round_nodes(t).tolist():
             outs[(n[0], n[1])] = o[n[4]:n[4] + n[5]].clone()

@@ -197,6 +197,11 @@ def test_device_calls_validate_before_launch():
     assert attn(cache_=_lib.KvCache(0x10000, 0x20000, 4, 2, 96, 128)) == _lib.WAVE_ERR_UNSUPPORTED
     assert attn(cache_=_lib.KvCache(0x10000, 0x20000, 4, 2, 64, 100)) == _lib.WAVE_ERR_INVALID_ARG
     assert attn(cache_=_lib.KvCache(0, 0x20000, 4, 2, 64, 128)) == _lib.WAVE_ERR_INVALID_ARG
+    # wave_attn_chain: wave_attn's checks, then a 4-byte aligned row_sq
+    assert lib.wave_attn_chain(pn.handle, fake, 5, C.byref(cache), fake, 0, 128, fake, None, 0.125, fake, None, 0,
+                               stream) == _lib.WAVE_ERR_INVALID_ARG
+    assert lib.wave_attn_chain(pn.handle, fake, 0, C.byref(cache), fake, 0, 128, fake, None, 0.125,
+                               C.c_void_p(0x10002), None, 0, stream) == _lib.WAVE_ERR_UNSUPPORTED
     # 32-bit per-lane V^T tile offsets: (head_dim-1)*lpad*2 + 128 must fit in int32
     lim128 = (2**31 - 1 - 128) // (127 * 2) // 64 * 64
     lim64 = (2**31 - 1 - 128) // (63 * 2) // 64 * 64
@@ -404,8 +409,8 @@ def test_chain_calls_validate_before_launch():
     assert b.value == int(pn.round_q_rows[1]) * 4
     assert lib.qkv_project_workspace(pn.handle, 99, C.byref(b)) == _lib.WAVE_ERR_INVALID_ARG
 
-    def proj(plan=pn, round_=1, cache_=cache, x=fake, layout=0, w=fake, q=fake, wsp=ws, nbytes=1 << 20):
-        return lib.qkv_project(plan.handle, fake, round_, C.byref(cache_), x, layout, w, q, wsp, nbytes, stream)
+    def proj(plan=pn, round_=1, cache_=cache, x=fake, layout=0, w=fake, q=fake, wsp=ws, nbytes=1 << 20, sq=None):
+        return lib.qkv_project(plan.handle, fake, round_, C.byref(cache_), x, layout, sq, w, q, wsp, nbytes, stream)
 
     assert proj(round_=9) == _lib.WAVE_ERR_INVALID_ARG
     assert proj(x=None) == _lib.WAVE_ERR_INVALID_ARG
@@ -413,6 +418,9 @@ def test_chain_calls_validate_before_launch():
     assert proj(q=C.c_void_p(0x10008)) == _lib.WAVE_ERR_UNSUPPORTED
     assert proj(wsp=None) == _lib.WAVE_ERR_INVALID_ARG
     assert proj(nbytes=4) == _lib.WAVE_ERR_CAPACITY
+    # per-head row statistics go with round-packed x only, and must be 4-byte aligned
+    assert proj(layout=1, sq=C.c_void_p(0x30000)) == _lib.WAVE_ERR_INVALID_ARG
+    assert proj(sq=C.c_void_p(0x30002)) == _lib.WAVE_ERR_UNSUPPORTED
     assert proj(cache_=_lib.KvCache(0x10000, 0x20000, pn.num_phys_slots, 1, 64, pn.lpad())) \
         == _lib.WAVE_ERR_UNSUPPORTED  # D = 64 is not a multiple of 128
     with_cond = native(4, 2, op.PROGRESSIVE, op.WAVE, -1, 128, 16)
