@@ -114,7 +114,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, choices=(2, 3, 4, 5, 6))
+    ap.add_argument("--workload", type=int, default=2, choices=(1, 2, 3, 4, 5, 6))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=768,
                     help="query rows per node for the CPU oracle (bounded sample, ~10-30 s of CPU work)")
@@ -159,6 +159,9 @@ def main():
     if args.workload == 3:
         print("workload 3 is a whole rollout: run it with --rollout", file=sys.stderr)
         sys.exit(2)
+    if args.workload == 1:
+        tiny_bench(args, device)
+        return
     out = measure_round(args, device, args.workload, args.steps, args.warmup, cpu=not args.no_cpu_baseline,
                         copy_calibration=args.copy_calibration)
     if args.workload == 2 and not args.no_extra:
@@ -519,6 +522,97 @@ def proj_bench(args, device):
                       "workload": w.name + "-qkv-projection", "unit": "TFLOP/s", "n_gpus": 1, "dtype": "bf16",
                       "data": "synthetic", "timing": "median of per-call event times, the two alternating",
                       "results": results}), flush=True)
+
+
+def tiny_bench(args, device):
+    """The tiny workload (B=4, K=2, 128-token chunks, 2 heads of 64, fp32 inputs)
+    as a whole: every round's kv_write + wave_attn on the GPU, timed per
+    rollout, beside the full fp64 CPU oracle of the same rollout (every node,
+    row and head), with the parity of the last GPU rollout against it.  Parity,
+    not throughput, is what this size shows."""
+    import torch
+    import block_causal_attention_wave_amd as wv
+    import wave_inputs as wi
+    from oracle import plan as op
+    from oracle.attention import round_to_bf16
+    from oracle.rollout import rollout
+    w = wi.WORKLOADS[1]
+    policy = w.policies[0]
+    plan = wv.wave_plan(B=w.B, K=w.K, policy=policy, sched=wv.WAVE, chunk_len=w.chunk_len, cond_len=w.cond_len)
+    desc = plan.upload(device)
+    cache = wv.KVCache(plan.num_phys_slots, w.heads, w.head_dim, plan.lpad(), device, fill=float("nan"))
+    host = {}
+
+    def host_in(c, lv, which):
+        if (c, lv, which) not in host:
+            host[(c, lv, which)] = wi.host_tensor(w, 0, c, lv, which, policy)
+        return host[(c, lv, which)]
+
+    rounds = []
+    for t in range(plan.num_rounds):
+        ws = plan.round_writes(t).tolist()
+        nodes = plan.round_nodes(t).tolist()
+        k = torch.from_numpy(np.concatenate([host_in(c, lv, "k") for (c, lv, _, _) in ws])).to(device)
+        v = torch.from_numpy(np.concatenate([host_in(c, lv, "v") for (c, lv, _, _) in ws])).to(device)
+        q = torch.from_numpy(np.concatenate([host_in(n[0], n[1], "q") for n in nodes])).to(device)
+        rows = int(plan.round_q_rows[t])
+        o = torch.empty((rows, w.heads, w.head_dim), dtype=torch.bfloat16, device=device)
+        lse = torch.empty((w.heads, rows), dtype=torch.float32, device=device)
+        rounds.append((t, k, v, q, o, lse, nodes))
+    stream = torch.cuda.Stream()
+    times = []
+    with torch.cuda.stream(stream):
+        for it in range(args.warmup + args.steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for (t, k, v, q, o, lse, _) in rounds:
+                wv.kv_write(plan, desc, t, cache, k, v, stream=stream)
+                wv.wave_attn(plan, desc, t, cache, q, w.scale, o=o, lse=lse, stream=stream)
+            e1.record(stream)
+            e1.synchronize()
+            if it >= args.warmup:
+                times.append(e0.elapsed_time(e1))
+    gpu_ms = float(np.median(times))
+    got = {}
+    for (t, k, v, q, o, lse, nodes) in rounds:
+        o_h, l_h = o.float().cpu().numpy(), lse.cpu().numpy()
+        for n in nodes:
+            got[(n[0], n[1])] = (o_h[n[4]:n[4] + n[5]], l_h[:, n[4]:n[4] + n[5]])
+    # The full oracle on the values the kernels consume (fp32 rounded to bf16, widened to fp64).
+    p = op.Params(w.B, w.K, policy, op.SERIAL, w.history_cap, w.chunk_len, w.cond_len, 0)
+    oplan = op.oracle_plan(p)
+    q64 = {key[:2]: round_to_bf16(x).astype(np.float64) for key, x in host.items() if key[2] == "q"}
+    kv64 = {key[:2]: (round_to_bf16(host[key[:2] + ("k",)]).astype(np.float64),
+                      round_to_bf16(host[key[:2] + ("v",)]).astype(np.float64))
+            for key in host if key[2] == "k"}
+    affinity = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", affinity))
+    t0 = time.perf_counter()
+    ref = rollout(p, oplan, lambda c, lv: q64[(c, lv)], lambda c, lv: kv64[(c, lv)], w.scale)
+    cpu_ms = (time.perf_counter() - t0) * 1e3
+    assert set(ref) == set(got)
+    err_o = max(float(np.abs(got[key][0] - ref[key][0]).max()) for key in ref)
+    err_l = max(float(np.abs(got[key][1] - ref[key][1]).max()) for key in ref)
+    flops = sum(algorithmic_flops(plan, t, w.heads, w.head_dim) for t in range(plan.num_rounds))
+    eprint(f"[bench] {w.name}: whole rollout ({plan.num_rounds} rounds, {len(ref)} nodes) {gpu_ms:.3f} ms on the "
+           f"GPU, {cpu_ms:.1f} ms for the full fp64 oracle ({threads} threads); max |dO| {err_o:.2e}, "
+           f"max |dLSE| {err_l:.2e}")
+    print(json.dumps({
+        "metric": "tiny workload: whole-rollout time, GPU beside the full CPU oracle (parity size)",
+        "value": round(gpu_ms, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "rounds": plan.num_rounds, "nodes": len(ref), "heads": w.heads,
+                   "head_dim": w.head_dim, "chunk_tokens": w.chunk_len, "src_dtype": "fp32",
+                   "algorithmic_gflop": round(flops / 1e9, 4)},
+        "parity": {"max_abs_o": err_o, "max_abs_lse": err_l},
+        "cpu_baseline": {"value": round(cpu_ms, 2), "unit": "ms", "cores": int(threads), "kind": "oracle",
+                         "affinity_cpus": affinity,
+                         "sample": "the whole rollout: every node, query row and head, fp64 dense masks"},
+    }), flush=True)
 
 
 def rollout_bench(args, device):
