@@ -461,7 +461,11 @@ def proj_bench(args, device):
     """qkv_project (RMS scaling, Q out, K/V^T into the node's cache slot) and
     the plain product x @ W^T of the same shape through torch.matmul, on the
     same box in one run: one round per distinct node count of the Wan2.1-1.3B
-    progressive plan, alternating the two, timed with events."""
+    progressive plan, alternating the three, timed with events.  qkv_project
+    runs twice: with 1/rms taken from x's rows (a separate row-scale launch
+    first) and with it formed from per-(row, head) sums of squares handed in,
+    as the chain hands over the ones its attention epilogue wrote (here they
+    are computed from x outside the timed calls)."""
     import torch
     import block_causal_attention_wave_amd as wv
     import wave_inputs as wi
@@ -489,20 +493,26 @@ def proj_bench(args, device):
             rows = int(plan.round_q_rows[t])
             x = x_all[:rows]
             flops = 2.0 * rows * D * 3 * D
+            sq = x.float().reshape(rows, w.heads, w.head_dim).square().sum(-1).contiguous()
 
             def proj():
                 wv.qkv_project(plan, desc, t, cache, x, weight, q=q[:rows], x_layout=wv.X_ROUND, workspace=ws,
                                stream=stream)
 
+            def proj_sq():
+                wv.qkv_project(plan, desc, t, cache, x, weight, q=q[:rows], x_layout=wv.X_ROUND, workspace=ws,
+                               stream=stream, row_sq=sq)
+
             def plain():
                 torch.matmul(x, weight_t, out=y[:rows])
 
+            fns = (("qkv_project", proj), ("qkv_project_rms_from_sq", proj_sq), ("torch.matmul", plain))
             for _ in range(warm):
-                proj()
-                plain()
-            times = {"qkv_project": [], "torch.matmul": []}
+                for _name, fn in fns:
+                    fn()
+            times = {name: [] for name, _fn in fns}
             for r in range(reps):
-                for name, fn in (("qkv_project", proj), ("torch.matmul", plain)):
+                for name, fn in fns:
                     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     e0.record(stream)
                     fn()
@@ -515,12 +525,14 @@ def proj_bench(args, device):
                 res[name + "_ms"] = round(med, 4)
                 res[name + "_tflops"] = round(flops / (med * 1e-3) / 1e12, 1)
             eprint(f"[proj] {count} nodes, {rows} rows: qkv_project {res['qkv_project_ms']:.4f} ms = "
-                   f"{res['qkv_project_tflops']:.0f} TFLOP/s; torch.matmul {res['torch.matmul_ms']:.4f} ms = "
+                   f"{res['qkv_project_tflops']:.0f} TFLOP/s; with the sums of squares handed in "
+                   f"{res['qkv_project_rms_from_sq_ms']:.4f} ms = {res['qkv_project_rms_from_sq_tflops']:.0f} "
+                   f"TFLOP/s; torch.matmul {res['torch.matmul_ms']:.4f} ms = "
                    f"{res['torch.matmul_tflops']:.0f} TFLOP/s")
             results.append(res)
     print(json.dumps({"metric": "qkv_project TFLOP/s against the plain product of the same shape",
                       "workload": w.name + "-qkv-projection", "unit": "TFLOP/s", "n_gpus": 1, "dtype": "bf16",
-                      "data": "synthetic", "timing": "median of per-call event times, the two alternating",
+                      "data": "synthetic", "timing": "median of per-call event times, the three alternating",
                       "results": results}), flush=True)
 
 
