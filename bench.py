@@ -460,7 +460,7 @@ def chain_bench(args, device):
 def proj_bench(args, device):
     """qkv_project (RMS scaling, Q out, K/V^T into the node's cache slot) and
     the plain product x @ W^T of the same shape through torch.matmul, on the
-    same box in one run: one round per distinct node count of the Wan2.1-1.3B
+    same GPU in one run: one round per distinct node count of the Wan2.1-1.3B
     progressive plan, alternating the three, timed with events.  qkv_project
     runs twice: with 1/rms taken from x's rows (a separate row-scale launch
     first) and with it formed from per-(row, head) sums of squares handed in,
